@@ -1,0 +1,200 @@
+"""Seeded synthetic inputs for exact softmax attention.
+
+This module only draws random numbers and lays them out.  It holds none of
+the attention arithmetic, so both the fp64 oracle (under ``oracle/``) and the
+HIP path can be fed from it without sharing any of the method.
+
+Inputs follow the workloads the pages describe: random Q/K/V in the
+``(B, N, H, d)`` layout of the fused-kernel example in "How to Reduce
+Attention Computation Cost in LLM Training" (section "FlashAttention Is Table
+Stakes"), head counts 32 query / 8 KV heads (same page, GQA/MQA section), a
+4096-token window (same page, sliding-window section), head size 64 with
+sequences up to 1024 ("Attention Is O(n^2)", section "Wall-Clock Impact of
+Tiling"), and caches of up to 32000 tokens ("Ch. 3: MHA Limitations, MQA, GQA,
+and FlashAttention", section 3.2).
+
+Recipe: ``numpy.random.default_rng(seed)``, ``standard_normal`` in float32,
+drawn in the order Q, K, V (each tensor drawn one batch index at a time, which
+yields the same stream as one draw).  bf16 tensors are rounded from those
+float32 values with round-to-nearest-even (torch's CPU cast).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+__all__ = [
+    "DenseConfig",
+    "PagedConfig",
+    "DENSE_CONFIGS",
+    "PAGED_CONFIGS",
+    "make_dense",
+    "make_paged",
+    "draw_normal",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class DenseConfig:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    window: int
+    dtype: str  # "bf16" or "f32"
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        # the fp32 value both sides use: 1/sqrt(d) rounded once to float32
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+@dataclasses.dataclass(frozen=True)
+class PagedConfig:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    len_lo: int
+    len_hi: int
+    window: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+# The five workloads: one fp32 single head, then the bf16 prefill shapes and
+# the paged decode shape.
+DENSE_CONFIGS = {
+    "f32_single_head_256": DenseConfig("f32_single_head_256", 1, 1, 1, 256, 256, 64,
+                                       False, 0, "f32", 0),
+    "mha_causal_8k": DenseConfig("mha_causal_8k", 4, 32, 32, 8192, 8192, 128,
+                                 True, 0, "bf16", 2),
+    "gqa_causal_16k": DenseConfig("gqa_causal_16k", 2, 32, 8, 16384, 16384, 128,
+                                  True, 0, "bf16", 3),
+    "mqa_causal_16k": DenseConfig("mqa_causal_16k", 2, 32, 1, 16384, 16384, 128,
+                                  True, 0, "bf16", 3),
+    "swa_causal_32k_w4096": DenseConfig("swa_causal_32k_w4096", 1, 32, 8, 32768, 32768,
+                                        128, True, 4096, "bf16", 4),
+}
+
+PAGED_CONFIGS = {
+    "paged_decode_16x32k": PagedConfig("paged_decode_16x32k", 16, 32, 8, 128, 16, 40000,
+                                       2000, 8000, 32000, 0, 5),
+}
+
+
+def draw_normal(rng: np.random.Generator, shape, chunk_axis0: bool = True) -> np.ndarray:
+    """float32 N(0,1) of ``shape`` drawn from ``rng``, one leading index at a time."""
+    out = np.empty(shape, dtype=np.float32)
+    if chunk_axis0 and len(shape) > 1:
+        for i in range(shape[0]):
+            out[i] = rng.standard_normal(shape[1:], dtype=np.float32)
+    else:
+        out[...] = rng.standard_normal(shape, dtype=np.float32)
+    return out
+
+
+def _to(x: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(x)
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)
+    if dtype == "f32":
+        return t
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_dense(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int,
+               dtype: str = "bf16"):
+    """Q [B,Nq,Hq,d], K and V [B,Nk,Hkv,d] as CPU torch tensors (bf16 or fp32)."""
+    rng = np.random.default_rng(seed)
+    q = _to(draw_normal(rng, (B, Nq, Hq, d)), dtype)
+    k = _to(draw_normal(rng, (B, Nk, Hkv, d)), dtype)
+    v = _to(draw_normal(rng, (B, Nk, Hkv, d)), dtype)
+    return q, k, v
+
+
+def make_dense_config(cfg: DenseConfig):
+    return make_dense(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, cfg.seed, cfg.dtype)
+
+
+def make_paged(B: int, Hq: int, Hkv: int, d: int, block_size: int, num_blocks: int,
+               max_blocks_per_seq: int, seed: int, len_lo: int = 1, len_hi: int = 1,
+               seq_lens=None, poison: bool = True):
+    """A block-paged KV cache with seeded contents.
+
+    Draw order: ``seq_lens`` (uniform integers in [len_lo, len_hi], unless given),
+    a permutation of the physical block ids, then q [B,Hq,d], then the K values
+    of every used slot in logical order (b, t, h, c), then the V values likewise.
+    Sequence b takes the next ceil(len_b / block_size) ids of the permutation.
+    Unused blocks and the unused tail slots of a sequence's last block hold NaN
+    when ``poison`` is set, so that reading one shows up in the result.
+
+    Returns a dict of CPU tensors: q (bf16), kcache, vcache (bf16,
+    [num_blocks, block_size, Hkv, d]), block_table (int32 [B, max_blocks_per_seq],
+    -1 past each sequence's end) and seq_lens (int32 [B]).
+    """
+    rng = np.random.default_rng(seed)
+    if seq_lens is None:
+        lens = rng.integers(len_lo, len_hi, size=B, endpoint=True).astype(np.int64)
+    else:
+        lens = np.asarray(seq_lens, dtype=np.int64)
+        if lens.shape != (B,):
+            raise ValueError("seq_lens must have B entries")
+    nblk = [(int(n) + block_size - 1) // block_size for n in lens]
+    if max(nblk, default=0) > max_blocks_per_seq:
+        raise ValueError("a sequence needs more blocks than max_blocks_per_seq")
+    if sum(nblk) > num_blocks:
+        raise ValueError("pool too small for the drawn lengths")
+    perm = rng.permutation(num_blocks)
+    table = np.full((B, max_blocks_per_seq), -1, dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        table[b, : nblk[b]] = perm[pos: pos + nblk[b]]
+        pos += nblk[b]
+    q = torch.from_numpy(rng.standard_normal((B, Hq, d), dtype=np.float32)).to(torch.bfloat16)
+
+    fill = float("nan") if poison else 0.0
+    caches = []
+    for _ in range(2):  # K then V
+        pool = torch.full((num_blocks, block_size, Hkv, d), fill, dtype=torch.bfloat16)
+        for b in range(B):
+            n = int(lens[b])
+            if n == 0:
+                continue
+            vals = torch.from_numpy(rng.standard_normal((n, Hkv, d), dtype=np.float32))
+            vals = vals.to(torch.bfloat16)
+            full, tail = divmod(n, block_size)
+            ids = torch.from_numpy(table[b, :full].astype(np.int64))
+            if full:
+                pool[ids] = vals[: full * block_size].reshape(full, block_size, Hkv, d)
+            if tail:
+                pool[int(table[b, full]), :tail] = vals[full * block_size:]
+        caches.append(pool)
+    return {
+        "q": q,
+        "kcache": caches[0],
+        "vcache": caches[1],
+        "block_table": torch.from_numpy(table),
+        "seq_lens": torch.from_numpy(lens.astype(np.int32)),
+    }
+
+
+def make_paged_config(cfg: PagedConfig, poison: bool = True):
+    return make_paged(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.block_size, cfg.num_blocks,
+                      cfg.max_blocks_per_seq, cfg.seed, cfg.len_lo, cfg.len_hi,
+                      poison=poison)
