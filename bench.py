@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * attn_fwd on the MHA causal prefill workload (B=4, Hq=Hkv=32, N=8192,
+    d=128, bf16), and
+  * attn_decode_paged on the paged decode workload (16 sequences of
+    8000..32000 cached tokens, Hq=32, Hkv=8, d=128, 16-token blocks in a
+    40000-block pool).
+
+Prints ONE JSON line.  `value` is the prefill throughput in TFLOP/s
+(causal-adjusted: 4*d FLOPs per visible query/key pair), timed with HIP events
+around each launch on the stream the kernels run on; the decode throughput in
+GB/s of algorithmic HBM bytes is reported beside it.  `roofline` is for the
+prefill kernel (bound: bf16 MFMA), `decode.roofline` for the decode kernels
+(bound: HBM).  `cpu_baseline` times the fp64 oracle on a bounded sample (two
+heads of the prefill workload) on the host cores and scales it to TFLOP/s.
+
+Other workloads can be timed with --workload NAME (one of the dense configs);
+the default line is the one described above.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak; paged decode HBM GB/s + % peak"
+PREFILL = "mha_causal_8k"
+DECODE = "paged_decode_16x32k"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "exact_softmax_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key, files):
+    """HBM bytes per launch from committed PMC counters, if they match the source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(key)
+    if not ent or ent.get("source_hash") != kernel_source_hash(files):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None,
+                    help="time only this dense workload's forward (extra lines)")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
+                    help="copy: a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(q, k, v, cfg):
+    """Time the fp64 oracle on two heads (all rows) and scale to TFLOP/s."""
+    import numpy as np
+    import oracle
+    from exact_softmax_attention_amd import metrics
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                        if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    heads = [(0, 0), (cfg.B - 1, cfg.Hq - 1)]
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, cfg.scale, cfg.causal, cfg.window, heads=heads)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * cfg.d * metrics.visible_pairs(cfg.Nq, cfg.Nk, cfg.causal, cfg.window) * len(heads)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(heads)} of {cfg.B * cfg.Hq} (batch, head) pairs of {cfg.name}, all "
+                      f"{cfg.Nq} rows, fp64 NumPy materialising S and P; {dt:.2f} s, scaled by "
+                      "causal-adjusted FLOPs",
+            "seconds": round(dt, 3), "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def time_loop(fns, steps, warmup, torch):
+    """Run each fn once per step; per-fn average ms from HIP events, total wall ms."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        for i, f in enumerate(fns):
+            f()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+           for i in range(len(fns))]
+    return per, wall
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU layout is described, not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from exact_softmax_attention_amd import attn_decode_paged, attn_fwd, metrics
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    if args.mode == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n,
+                          "launches": max(1, args.steps)}))
+        return
+
+    name = args.workload or PREFILL
+    cfg = workloads.DENSE_CONFIGS[name]
+    print(f"bench: generating {name}", file=sys.stderr, flush=True)
+    q, k, v = workloads.make_dense_config(cfg)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    if cfg.dtype != "bf16":
+        raise SystemExit("bench: the prefill line is the bf16 kernel")
+    out = torch.empty_like(qd)
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.Nq), dtype=torch.float32, device=dev)
+
+    def fwd():
+        attn_fwd(qd, kd, vd, causal=cfg.causal, window=cfg.window, scale=cfg.scale, out=out,
+                 lse=lse)
+
+    fns = [fwd]
+    dec = None
+    if args.workload is None:
+        pc = workloads.PAGED_CONFIGS[DECODE]
+        print(f"bench: generating {DECODE}", file=sys.stderr, flush=True)
+        inp = workloads.make_paged_config(pc)
+        dd = {kk: t.to(dev) for kk, t in inp.items()}
+        dout = torch.empty_like(dd["q"])
+        dlse = torch.empty(dd["q"].shape[:2], dtype=torch.float32, device=dev)
+        from exact_softmax_attention_amd import attn_decode_paged_workspace_size
+        ws = torch.empty(attn_decode_paged_workspace_size(pc.B, pc.Hq, pc.d, pc.block_size,
+                                                          pc.max_blocks_per_seq),
+                         dtype=torch.uint8, device=dev)
+
+        def decode():
+            attn_decode_paged(dd["q"], dd["kcache"], dd["vcache"], dd["block_table"],
+                              dd["seq_lens"], scale=pc.scale, out=dout, lse=dlse, workspace=ws)
+
+        fns.append(decode)
+        dec = (pc, inp["seq_lens"].numpy())
+
+    print("bench: timing", file=sys.stderr, flush=True)
+    per, wall = time_loop(fns, args.steps, args.warmup, torch)
+
+    flops = metrics.fwd_flops(cfg.B, cfg.Hq, cfg.Nq, cfg.Nk, cfg.d, cfg.causal, cfg.window)
+    fwd_ms = per[0]
+    tflops = flops / (fwd_ms * 1e-3) / 1e12
+    fwd_files = ["fwd_bf16.hip", "device_common.h"]
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sum(per), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name if dec is None else f"{name}+{DECODE}",
+                   "prefill": {"name": name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+                               "N": cfg.Nq, "d": cfg.d, "causal": cfg.causal,
+                               "window": cfg.window, "seed": cfg.seed}},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / metrics.PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(f"fwd:{name}", fwd_files),
+                     "kernel": "fwd_bf16_kernel<128>", "ms": round(fwd_ms, 4),
+                     "flop_per_launch": flops,
+                     "algorithmic_bytes": metrics.fwd_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq,
+                                                            cfg.Nk, cfg.d)},
+        "wall_ms_per_step": round(wall, 4),
+    }
+    if dec is not None:
+        pc, lens = dec
+        nbytes = metrics.decode_bytes(lens, pc.Hq, pc.Hkv, pc.d, pc.block_size)
+        gbs = nbytes / (per[1] * 1e-3) / 1e9
+        res["config"]["decode"] = {"name": pc.name, "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv,
+                                   "d": pc.d, "block_size": pc.block_size,
+                                   "num_blocks": pc.num_blocks, "seq_lens_sum": int(lens.sum()),
+                                   "seed": pc.seed}
+        res["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "ms": round(per[1], 4),
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                      "peak": metrics.PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(gbs / metrics.PEAK_HBM_GBS, 4),
+                                      "traffic": measured_traffic(f"decode:{pc.name}",
+                                                                  ["decode_paged.hip",
+                                                                   "device_common.h"]),
+                                      "kernels": "decode_split_kernel<4,128> + "
+                                                 "decode_combine_kernel<128>",
+                                      "algorithmic_bytes": nbytes}}
+    if not args.skip_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(q, k, v, cfg)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+"""Exact softmax attention for MI355X (gfx950): thin Python binding.
+
+The functions here only marshal arguments: they check dtypes, devices and
+contiguity, allocate outputs with torch, and call the C ABI of libattn.so
+(``include/attn.h``) on torch's current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+
+    attn_fwd(q, k, v, causal=False, window=0, scale=None)        bf16 prefill
+    attn_fwd_f32(q, k, v, causal=False, window=0, scale=None)    fp32 prefill
+    attn_decode_paged(q, kcache, vcache, block_table, seq_lens, ...)
+    attn_decode_paged_workspace_size(B, Hq, d, block_size, max_blocks_per_seq)
+    attn_status_str(code)
+
+Layouts: q [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d]; out like q; lse [B, Hq, Nq]
+float32.  Decode: q [B, Hq, d]; caches [num_blocks, block_size, Hkv, d];
+block_table [B, max_blocks] int32; seq_lens [B] int32; out [B, Hq, d];
+lse [B, Hq].
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "attn_fwd",
+    "attn_fwd_f32",
+    "attn_decode_paged",
+    "attn_decode_paged_workspace_size",
+    "attn_status_str",
+    "AttnError",
+]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {_lib.status_str(code)} (status {code})")
+
+
+def attn_status_str(code: int) -> str:
+    return _lib.status_str(code)
+
+
+def _check(code: int, where: str):
+    if code == _lib.ATTN_OK:
+        return
+    if code in (_lib.ATTN_E_SHAPE, _lib.ATTN_E_HEADDIM, _lib.ATTN_E_MASK, _lib.ATTN_E_NULL,
+                _lib.ATTN_E_WORKSPACE):
+        raise ValueError(f"{where}: {_lib.status_str(code)} (status {code})")
+    raise AttnError(code, where)
+
+
+def _dev(t: torch.Tensor, name: str, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _fwd(fn_name, dtype, q, k, v, causal, window, scale, out, lse, return_lse):
+    _dev(q, "q", dtype)
+    _dev(k, "k", dtype)
+    _dev(v, "v", dtype)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Nq,Hq,d], k and v [B,Nk,Hkv,d]")
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError("q and k disagree on batch or head dimension")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", dtype)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if lse.shape != (B, Hq, Nq):
+            raise ValueError("lse must be [B, Hq, Nq]")
+    fn = getattr(_lib.lib(), fn_name)
+    code = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+              lse.data_ptr() if lse is not None else None,
+              B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), int(window), float(scale),
+              _stream(q.device))
+    _check(code, fn_name)
+    return out, lse
+
+
+def attn_fwd(q, k, v, causal: bool = False, window: int = 0, scale=None, out=None, lse=None,
+             return_lse: bool = True):
+    """bf16 attention forward.  Returns (out, lse); lse is None if not requested."""
+    return _fwd("attn_fwd", torch.bfloat16, q, k, v, causal, window, scale, out, lse, return_lse)
+
+
+def attn_fwd_f32(q, k, v, causal: bool = False, window: int = 0, scale=None, out=None, lse=None,
+                 return_lse: bool = True):
+    """float32 attention forward.  Returns (out, lse)."""
+    return _fwd("attn_fwd_f32", torch.float32, q, k, v, causal, window, scale, out, lse,
+                return_lse)
+
+
+def attn_decode_paged_workspace_size(B: int, Hq: int, d: int, block_size: int,
+                                     max_blocks_per_seq: int) -> int:
+    return int(_lib.lib().attn_decode_paged_workspace_size(B, Hq, d, block_size,
+                                                           max_blocks_per_seq))
+
+
+def attn_decode_paged(q, kcache, vcache, block_table, seq_lens, scale=None, window: int = 0,
+                      out=None, lse=None, workspace=None, return_lse: bool = True):
+    """Single-query decode over a paged cache.  Returns (out, lse)."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(kcache, "kcache", torch.bfloat16)
+    _dev(vcache, "vcache", torch.bfloat16)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 3 or kcache.dim() != 4 or vcache.shape != kcache.shape:
+        raise ValueError("expected q [B,Hq,d] and caches [num_blocks,block_size,Hkv,d]")
+    B, Hq, d = q.shape
+    num_blocks, block_size, Hkv, dk = kcache.shape
+    if dk != d:
+        raise ValueError("q and the cache disagree on the head dimension")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    max_blocks = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    need = attn_decode_paged_workspace_size(B, Hq, d, block_size, max_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device.type != "cuda":
+        raise ValueError("workspace must be on the GPU")
+    code = _lib.lib().attn_decode_paged(
+        q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        B, Hq, Hkv, d, block_size, max_blocks, num_blocks, int(window), float(scale),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(code, "attn_decode_paged")
+    return out, lse

@@ -1,0 +1,110 @@
+// C ABI of the attention library: argument validation, then dispatch to the
+// gfx950 kernels.  Validation runs entirely on the host before any HIP call.
+#include "attn.h"
+
+#include <climits>
+
+#include "launch.h"
+
+namespace {
+
+int check_common(int B, int Hq, int Hkv, int d) {
+  if (B < 0 || Hq < 1 || Hkv < 1) return ATTN_E_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_E_SHAPE;
+  if (d != 64 && d != 128) return ATTN_E_HEADDIM;
+  return ATTN_OK;
+}
+
+int check_fwd(const void* q, const void* k, const void* v, const void* out, int B, int Hq,
+              int Hkv, int Nq, int Nk, int d, int causal, int window, long long grid) {
+  int st = check_common(B, Hq, Hkv, d);
+  if (st != ATTN_OK) return st;
+  if (Nq < 0 || Nk < 0) return ATTN_E_SHAPE;
+  // pointers of empty tensors may be NULL
+  if ((long long)B * Nq > 0 && (!q || !out)) return ATTN_E_NULL;
+  if ((long long)B * Nk > 0 && (!k || !v)) return ATTN_E_NULL;
+  if (causal != 0 && causal != 1) return ATTN_E_MASK;
+  if (window > 0 && !causal) return ATTN_E_MASK;
+  if (causal && Nq > Nk) return ATTN_E_SHAPE;
+  if (grid > INT_MAX) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+int fwd_common(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+               int Hkv, int Nq, int Nk, int d, int causal, int window, float scale, void* stream,
+               bool f32) {
+  const long long grid =
+      (B >= 0 && Hq >= 1 && Nq >= 0)
+          ? (f32 ? attn::fwd_f32_grid(B, Hq, Nq) : attn::fwd_bf16_grid(B, Hq, Nq))
+          : 0;
+  const int st = check_fwd(q, k, v, out, B, Hq, Hkv, Nq, Nk, d, causal, window, grid);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  attn::FwdArgs a{q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, causal, window > 0 ? window : 0,
+                  scale};
+  const hipError_t e = f32 ? attn::launch_fwd_f32(a, static_cast<hipStream_t>(stream))
+                           : attn::launch_fwd_bf16(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+             int Hkv, int Nq, int Nk, int d, int causal, int window, float scale, void* stream) {
+  return fwd_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, stream,
+                    false);
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse, int B,
+                 int Hq, int Hkv, int Nq, int Nk, int d, int causal, int window, float scale,
+                 void* stream) {
+  return fwd_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, stream,
+                    true);
+}
+
+size_t attn_decode_paged_workspace_size(int B, int Hq, int d, int block_size,
+                                        int max_blocks_per_seq) {
+  if (B < 0 || Hq < 1 || (d != 64 && d != 128) || block_size != 16 || max_blocks_per_seq < 1)
+    return 0;
+  if ((long long)max_blocks_per_seq * block_size > INT_MAX) return 0;
+  return attn::decode_workspace_bytes(B, Hq, d, block_size, max_blocks_per_seq);
+}
+
+int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
+                      const int* block_table, const int* seq_lens, void* out, float* lse, int B,
+                      int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
+                      int num_blocks, int window, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_common(B, Hq, Hkv, d);
+  if (st != ATTN_OK) return st;
+  if (B > 0 && (!q || !kcache || !vcache || !block_table || !seq_lens || !out))
+    return ATTN_E_NULL;
+  if (block_size != 16 || max_blocks_per_seq < 1 || num_blocks < 1) return ATTN_E_SHAPE;
+  if ((long long)max_blocks_per_seq * block_size > INT_MAX) return ATTN_E_SHAPE;
+  if (B > 65535 || Hq > 65535) return ATTN_E_SHAPE;  // grid y / z limits
+  if (B == 0) return ATTN_OK;
+  const size_t need = attn::decode_workspace_bytes(B, Hq, d, block_size, max_blocks_per_seq);
+  if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
+  attn::DecodeArgs a{q,  kcache, vcache, block_table, seq_lens, out, lse,
+                     B,  Hq,     Hkv,    d,           block_size, max_blocks_per_seq,
+                     num_blocks, window > 0 ? window : 0, scale, workspace};
+  const hipError_t e = attn::launch_decode_paged(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULL: return "a required pointer is NULL";
+    case ATTN_E_SHAPE: return "invalid or unsupported sizes";
+    case ATTN_E_HEADDIM: return "head dimension must be 64 or 128";
+    case ATTN_E_MASK: return "invalid mask (window requires causal; causal is 0 or 1)";
+    case ATTN_E_WORKSPACE: return "workspace missing or too small";
+    case ATTN_E_LAUNCH: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, d;
+  int causal, window;
+  float scale;
+};
+
+// Both assume arguments already validated (d in {64,128}, Hq % Hkv == 0, ...).
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+// Work groups the forward launch uses (for the grid-size check).
+long long fwd_bf16_grid(int B, int Hq, int Nq);
+long long fwd_f32_grid(int B, int Hq, int Nq);
+
+struct DecodeArgs {
+  const void* q;
+  const void* kcache;
+  const void* vcache;
+  const int* block_table;
+  const int* seq_lens;
+  void* out;
+  float* lse;
+  int B, Hq, Hkv, d, block_size, max_blocks_per_seq, num_blocks, window;
+  float scale;
+  void* workspace;
+};
+
+size_t decode_workspace_bytes(int B, int Hq, int d, int block_size, int max_blocks_per_seq);
+hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace attn

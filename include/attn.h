@@ -1,0 +1,147 @@
+/*
+ * attn.h — C ABI of the MI355X (gfx950) exact softmax attention library.
+ *
+ * Two operations, both exact (up to floating-point rounding order) scaled
+ * dot-product attention O = softmax(scale * Q K^T + mask) V:
+ *
+ *   attn_fwd / attn_fwd_f32  prefill / training forward over dense Q, K, V,
+ *                            tiled and fused with an online softmax so the
+ *                            score matrix never reaches device memory, with
+ *                            causal and sliding-window masks and grouped
+ *                            K/V heads (MHA, GQA, MQA);
+ *   attn_decode_paged        one query per sequence over a block-paged KV
+ *                            cache, split along the keys with a final merge.
+ *
+ * Sources (pages; section names as printed):
+ *   - "Attention Is O(n^2): FlashAttention vs Linear Attention", "Why
+ *     Attention Is O(n^2)" (the definition) and "FlashAttention - Same
+ *     FLOPs, Linear Memory" (query-block / key-block loop with a running
+ *     maximum and sum, final normalisation, float32 log-sum-exp kept for the
+ *     backward pass).
+ *   - "Ch. 3: MHA Limitations, MQA, GQA, and FlashAttention", 3.3 (query head
+ *     i reads K/V head i / (Hq / Hkv); Hq must be a multiple of Hkv), 3.5
+ *     (merging partial softmax statistics across key tiles), 3.1 (decode: a
+ *     new query reads the cached K/V, its own K/V appended first).
+ *   - "Modern Attention: MQA, GQA, FlashAttention, Sliding Window and RoPE",
+ *     3 (online softmax) and 4 (a token sees the last W tokens).
+ *   - "Inference Engineering", 2.5 "Optimizing Attention" (PagedAttention:
+ *     the cache is split into blocks reached through a lookup table).
+ *   - "How to Reduce Attention Computation Cost in LLM Training",
+ *     "FlashAttention Is Table Stakes" (fused call on (B, N, H, d) bf16).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; nothing is
+ *     retained after the call returns.  Tensors are dense, row-major, with no
+ *     padding.  Outputs must not alias inputs.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL means the default stream).  The library never synchronises and
+ *     never allocates device memory.
+ *   - Arguments are validated on the host before any HIP call; a negative
+ *     status is returned and nothing is launched.  Values that live in device
+ *     memory (sequence lengths, block ids) are checked by the kernels, which
+ *     write NaN for a sequence they cannot read safely and never read out of
+ *     bounds.
+ *   - Masks (reading of the pages where they are silent):
+ *       causal:  query row i sits at absolute position i + (Nk - Nq)
+ *                ("bottom-right"), and sees keys j <= that position;
+ *       window:  W > 0 keeps the last W keys up to and including the query's
+ *                own position (position - j < W); it requires causal.
+ *     A query row that sees no key gets O = 0 and LSE = -inf.
+ *   - LSE is the natural logarithm of sum_j exp(scale * q.k_j) over the
+ *     visible keys, in float32.
+ *   - `scale` is used as given (callers normally pass 1/sqrt(d)).
+ *   - The library is thread-safe and keeps no state between calls.
+ */
+#ifndef ATTN_MI355X_ATTN_H
+#define ATTN_MI355X_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = -1,      /* a required pointer is NULL                          */
+  ATTN_E_SHAPE = -2,     /* bad size: negative, Hq % Hkv != 0, causal with      */
+                         /* Nq > Nk, unsupported block size, grid too large     */
+  ATTN_E_HEADDIM = -3,   /* head dimension d not in {64, 128}                   */
+  ATTN_E_MASK = -4,      /* window > 0 without causal                           */
+  ATTN_E_WORKSPACE = -5, /* workspace NULL or smaller than the query says       */
+  ATTN_E_LAUNCH = -6     /* the HIP runtime reported an error at launch         */
+};
+
+/*
+ * Prefill / training forward, bf16 in and out, float32 accumulation.
+ *
+ *   q    [B, Nq, Hq, d]   bf16
+ *   k, v [B, Nk, Hkv, d]  bf16
+ *   out  [B, Nq, Hq, d]   bf16 (rounded to nearest even)
+ *   lse  [B, Hq, Nq]      float32, or NULL to skip it
+ *
+ * Sizes: B, Nq, Nk >= 0 (B == 0 or Nq == 0 is a no-op; Nk == 0 gives O = 0,
+ * LSE = -inf); Hq, Hkv >= 1 with Hq % Hkv == 0; d in {64, 128}.  Pointers of
+ * tensors with no elements may be NULL; the others must not be (ATTN_E_NULL).
+ * causal: 0 or 1; causal requires Nq <= Nk.  window: <= 0 for none, else the
+ * number of keys kept (requires causal).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d,
+             int causal, int window, float scale, void* stream);
+
+/*
+ * The same operation on float32 q, k, v and out, with float32 products and
+ * accumulation throughout (no reduced-precision matrix formats).  Parameters
+ * and rules are those of attn_fwd.
+ */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 int causal, int window, float scale, void* stream);
+
+/*
+ * Bytes of device workspace attn_decode_paged needs for these sizes
+ * (0 for invalid sizes).  Pure host function; no HIP call.
+ */
+size_t attn_decode_paged_workspace_size(int B, int Hq, int d, int block_size,
+                                        int max_blocks_per_seq);
+
+/*
+ * Single-query decode over a block-paged KV cache.
+ *
+ *   q            [B, Hq, d] bf16: the query of the token at position
+ *                seq_lens[b] - 1, whose own K/V are already in the cache
+ *   kcache,
+ *   vcache       [num_blocks, block_size, Hkv, d] bf16
+ *   block_table  [B, max_blocks_per_seq] int32: logical token t of sequence b
+ *                is slot t % block_size of block block_table[b][t / block_size];
+ *                entries past ceil(seq_lens[b] / block_size) are ignored
+ *   seq_lens     [B] int32, cached tokens per sequence (device memory)
+ *   out          [B, Hq, d] bf16
+ *   lse          [B, Hq] float32, or NULL
+ *   window       <= 0: attend every cached token; else the last `window`
+ *   workspace    device scratch of at least
+ *                attn_decode_paged_workspace_size(...) bytes, owned by the
+ *                caller; its contents on entry do not matter
+ *
+ * block_size must be 16; d in {64, 128}; Hq % Hkv == 0.  A sequence with
+ * seq_len == 0 gets O = 0, LSE = -inf.  A sequence whose length is negative or
+ * exceeds max_blocks_per_seq * block_size, or whose table names a block
+ * outside [0, num_blocks), gets NaN in out and lse.  Only the used slots of the
+ * cache are read; unused blocks and tail slots may hold anything (NaN too).
+ */
+int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
+                      const int* block_table, const int* seq_lens, void* out, float* lse,
+                      int B, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
+                      int num_blocks, int window, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_ATTN_H */

@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports what include/attn.h declares, and rejects
+bad arguments on the host (no GPU needed: validation runs before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_softmax_attention_amd import _lib
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "attn.h")
+FAKE = 0x1000  # a non-NULL pointer that is never dereferenced: every call below fails validation
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared()
+    assert declared == sorted(_lib.SIGNATURES)
+    lib = ctypes.CDLL(_lib.library_path())
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name in ("ATTN_OK", "ATTN_E_NULL", "ATTN_E_SHAPE", "ATTN_E_HEADDIM", "ATTN_E_MASK",
+                 "ATTN_E_WORKSPACE", "ATTN_E_LAUNCH"):
+        val = int(re.search(rf"\b{name}\s*=\s*(-?\d+)", text).group(1))
+        assert getattr(_lib, name) == val
+        assert _lib.status_str(val)
+    assert _lib.status_str(12345) == "unknown status"
+
+
+def _fwd(fn="attn_fwd", ptr=FAKE, lse=None, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, causal=0,
+         window=0):
+    return getattr(_lib.lib(), fn)(ptr, ptr, ptr, ptr, lse, B, Hq, Hkv, Nq, Nk, d, causal,
+                                   window, 0.125, None)
+
+
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_f32"])
+def test_fwd_validation(fn):
+    assert _fwd(fn, ptr=None) == _lib.ATTN_E_NULL
+    assert _fwd(fn, Hq=3, Hkv=2) == _lib.ATTN_E_SHAPE          # Hq % Hkv
+    assert _fwd(fn, Hkv=0) == _lib.ATTN_E_SHAPE
+    assert _fwd(fn, B=-1) == _lib.ATTN_E_SHAPE
+    assert _fwd(fn, Nq=-1) == _lib.ATTN_E_SHAPE
+    assert _fwd(fn, d=96) == _lib.ATTN_E_HEADDIM
+    assert _fwd(fn, d=256) == _lib.ATTN_E_HEADDIM
+    assert _fwd(fn, window=4) == _lib.ATTN_E_MASK               # window needs causal
+    assert _fwd(fn, causal=2) == _lib.ATTN_E_MASK
+    assert _fwd(fn, causal=1, Nq=9, Nk=8) == _lib.ATTN_E_SHAPE  # causal with Nq > Nk
+    assert _fwd(fn, B=1 << 20, Hq=1 << 10, Nq=1 << 20) == _lib.ATTN_E_SHAPE  # grid too large
+    # empty problems are accepted without touching memory (no launch happens)
+    assert _fwd(fn, ptr=None, B=0) == _lib.ATTN_OK
+    assert _fwd(fn, ptr=None, Nq=0, Nk=0) == _lib.ATTN_OK
+
+
+def test_decode_workspace_size():
+    L = _lib.lib()
+    n = L.attn_decode_paged_workspace_size(16, 32, 128, 16, 2000)
+    # one (m, l) pair and d floats per (sequence, query head, 256-token split)
+    slots = 16 * 32 * 125
+    assert n >= slots * (128 * 4 + 8)
+    assert n < slots * (128 * 4 + 8) + 512
+    assert L.attn_decode_paged_workspace_size(16, 32, 128, 32, 2000) == 0   # block size
+    assert L.attn_decode_paged_workspace_size(16, 32, 96, 16, 2000) == 0    # head dim
+    assert L.attn_decode_paged_workspace_size(16, 32, 64, 16, 0) == 0
+
+
+def _dec(ptr=FAKE, B=2, Hq=8, Hkv=2, d=128, bs=16, maxb=10, nb=100, window=0, ws=FAKE,
+         ws_bytes=1 << 30):
+    return _lib.lib().attn_decode_paged(ptr, ptr, ptr, ptr, ptr, ptr, None, B, Hq, Hkv, d, bs,
+                                        maxb, nb, window, 0.1, ws, ws_bytes, None)
+
+
+def test_decode_validation():
+    assert _dec(ptr=None) == _lib.ATTN_E_NULL
+    assert _dec(Hq=6, Hkv=4) == _lib.ATTN_E_SHAPE
+    assert _dec(d=32) == _lib.ATTN_E_HEADDIM
+    assert _dec(bs=8) == _lib.ATTN_E_SHAPE
+    assert _dec(maxb=0) == _lib.ATTN_E_SHAPE
+    assert _dec(nb=0) == _lib.ATTN_E_SHAPE
+    assert _dec(ws=None) == _lib.ATTN_E_WORKSPACE
+    need = _lib.lib().attn_decode_paged_workspace_size(2, 8, 128, 16, 10)
+    assert _dec(ws_bytes=need - 1) == _lib.ATTN_E_WORKSPACE
+    assert _dec(ptr=None, B=0) == _lib.ATTN_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        _lib.lib()

@@ -13,15 +13,21 @@ sequences up to 1024 ("Attention Is O(n^2)", section "Wall-Clock Impact of
 Tiling"), and caches of up to 32000 tokens ("Ch. 3: MHA Limitations, MQA, GQA,
 and FlashAttention", section 3.2).
 
-Recipe: ``numpy.random.default_rng(seed)``, ``standard_normal`` in float32,
-drawn in the order Q, K, V (each tensor drawn one batch index at a time, which
-yields the same stream as one draw).  bf16 tensors are rounded from those
-float32 values with round-to-nearest-even (torch's CPU cast).
+Recipe: every tensor is viewed as rows of its last two dimensions' product
+(e.g. [B*N, H*d]) and cut into fixed chunks of ``CHUNK_ROWS`` rows; chunk c of
+tensor number t (Q = 0, K = 1, V = 2; for the paged cache K = 1, V = 2 per
+sequence) is drawn with ``numpy.random.default_rng`` seeded by child c of
+``SeedSequence([seed, t])``, ``standard_normal`` in float32.  The chunks are
+independent, so they are drawn on several threads and the values do not
+depend on the thread count.  bf16 tensors are rounded from those float32
+values with round-to-nearest-even (torch's CPU cast).
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 
 import numpy as np
 import torch
@@ -98,15 +104,35 @@ PAGED_CONFIGS = {
 }
 
 
-def draw_normal(rng: np.random.Generator, shape, chunk_axis0: bool = True) -> np.ndarray:
-    """float32 N(0,1) of ``shape`` drawn from ``rng``, one leading index at a time."""
-    out = np.empty(shape, dtype=np.float32)
-    if chunk_axis0 and len(shape) > 1:
-        for i in range(shape[0]):
-            out[i] = rng.standard_normal(shape[1:], dtype=np.float32)
-    else:
-        out[...] = rng.standard_normal(shape, dtype=np.float32)
-    return out
+CHUNK_ROWS = 4096
+_THREADS = min(16, os.cpu_count() or 1)
+
+
+def _child_rngs(key, n: int):
+    return [np.random.default_rng(s) for s in np.random.SeedSequence(list(key)).spawn(n)]
+
+
+def draw_normal(seed: int, tag: int, shape, sub=None) -> np.ndarray:
+    """float32 N(0,1) of ``shape``; chunk c of CHUNK_ROWS rows uses child c of
+    SeedSequence([seed, tag]) (or [seed, tag, sub])."""
+    shape = tuple(int(x) for x in shape)
+    cols = int(np.prod(shape[-2:])) if len(shape) >= 2 else 1
+    rows = int(np.prod(shape)) // cols if cols else 0
+    out = np.empty((rows, cols), dtype=np.float32)
+    nchunks = (rows + CHUNK_ROWS - 1) // CHUNK_ROWS
+    rngs = _child_rngs([seed, tag] + ([] if sub is None else [sub]), nchunks)
+
+    def fill(c):
+        r0 = c * CHUNK_ROWS
+        r1 = min(rows, r0 + CHUNK_ROWS)
+        out[r0:r1] = rngs[c].standard_normal((r1 - r0, cols), dtype=np.float32)
+
+    if nchunks > 1:
+        with cf.ThreadPoolExecutor(max_workers=_THREADS) as ex:
+            list(ex.map(fill, range(nchunks)))
+    elif nchunks == 1:
+        fill(0)
+    return out.reshape(shape)
 
 
 def _to(x: np.ndarray, dtype: str) -> torch.Tensor:
@@ -121,10 +147,9 @@ def _to(x: np.ndarray, dtype: str) -> torch.Tensor:
 def make_dense(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int,
                dtype: str = "bf16"):
     """Q [B,Nq,Hq,d], K and V [B,Nk,Hkv,d] as CPU torch tensors (bf16 or fp32)."""
-    rng = np.random.default_rng(seed)
-    q = _to(draw_normal(rng, (B, Nq, Hq, d)), dtype)
-    k = _to(draw_normal(rng, (B, Nk, Hkv, d)), dtype)
-    v = _to(draw_normal(rng, (B, Nk, Hkv, d)), dtype)
+    q = _to(draw_normal(seed, 0, (B, Nq, Hq, d)), dtype)
+    k = _to(draw_normal(seed, 1, (B, Nk, Hkv, d)), dtype)
+    v = _to(draw_normal(seed, 2, (B, Nk, Hkv, d)), dtype)
     return q, k, v
 
 
@@ -137,9 +162,11 @@ def make_paged(B: int, Hq: int, Hkv: int, d: int, block_size: int, num_blocks: i
                seq_lens=None, poison: bool = True):
     """A block-paged KV cache with seeded contents.
 
-    Draw order: ``seq_lens`` (uniform integers in [len_lo, len_hi], unless given),
-    a permutation of the physical block ids, then q [B,Hq,d], then the K values
-    of every used slot in logical order (b, t, h, c), then the V values likewise.
+    From ``default_rng(seed)``, in order: ``seq_lens`` (uniform integers in
+    [len_lo, len_hi], unless given), a permutation of the physical block ids,
+    then q [B,Hq,d].  The K values of sequence b's used slots, in logical order
+    (t, h, c), come from ``draw_normal(seed, 1, (len_b, Hkv, d), sub=b)`` and
+    the V values from tag 2 likewise.
     Sequence b takes the next ceil(len_b / block_size) ids of the permutation.
     Unused blocks and the unused tail slots of a sequence's last block hold NaN
     when ``poison`` is set, so that reading one shows up in the result.
@@ -170,13 +197,13 @@ def make_paged(B: int, Hq: int, Hkv: int, d: int, block_size: int, num_blocks: i
 
     fill = float("nan") if poison else 0.0
     caches = []
-    for _ in range(2):  # K then V
+    for tag in (1, 2):  # K then V
         pool = torch.full((num_blocks, block_size, Hkv, d), fill, dtype=torch.bfloat16)
         for b in range(B):
             n = int(lens[b])
             if n == 0:
                 continue
-            vals = torch.from_numpy(rng.standard_normal((n, Hkv, d), dtype=np.float32))
+            vals = torch.from_numpy(draw_normal(seed, tag, (n, Hkv, d), sub=b))
             vals = vals.to(torch.bfloat16)
             full, tail = divmod(n, block_size)
             ids = torch.from_numpy(table[b, :full].astype(np.int64))
