@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -45,19 +46,46 @@ def common_flags():
     ]
 
 
-def _compile(src: str) -> str:
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                     r"Occupancy \[waves/SIMD\]|LDS Size \[bytes/block\]):\s+(\S+)")
+
+
+def _resources(stderr: str):
+    """Per-kernel resource usage from the compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for key, val in _REMARK.findall(stderr):
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key.split(" ")[0]] = int(val)
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags() + ["-Rpass-analysis=kernel-resource-usage",
+                                        "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
-    return obj
+    usage = _resources(res.stderr)
+    # A kernel that spills or keeps arrays in scratch memory is a build error:
+    # it is always a performance bug in these kernels.
+    bad = {k: v for k, v in usage.items() if v.get("ScratchSize", 0) > 0}
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch memory: {bad}")
+    return obj, usage
 
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(_compile, SOURCES))
+    objs = [o for o, _ in results]
+    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+        for _, usage in results:
+            for name, u in sorted(usage.items()):
+                f.write(f"{name}: {u}\n")
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)

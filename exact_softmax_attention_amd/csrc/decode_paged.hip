@@ -107,16 +107,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
   const int64_t row_elems = (int64_t)p.Hkv * D;  // one token's row of the pool
   bool bad = false;
 
-  u32x4 kr[2][2][NV], vr[2][2][NV];  // [buffer][pass][piece]
-  auto fetch = [&](int i, int buf) {
-    const int phys = trow[i];
+  // K/V registers of one block, [pass][piece]: `ck/cv` are being computed
+  // while the next block's loads land in `nk/nv`.  Only static indices, and no
+  // branch around the loads, so that everything stays in registers.  A block
+  // id outside the pool is replaced by block 0 (an in-bounds read) and the
+  // split is flagged, which makes the whole sequence NaN.
+  u32x4 ck[2][NV], cv[2][NV], nk[2][NV], nv[2][NV];
+  auto fetch = [&](int i, u32x4 (&rk)[2][NV], u32x4 (&rv)[2][NV]) {
+    int phys = trow[i];
     if (phys < 0 || phys >= p.num_blocks) {
       bad = true;
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass)
-#pragma unroll
-        for (int c = 0; c < NV; ++c) kr[buf][pass][c] = vr[buf][pass][c] = u32x4{0u, 0u, 0u, 0u};
-      return;
+      phys = 0;
     }
     const int64_t base = ((int64_t)phys * kBlock) * row_elems + (int64_t)hk * D + part * DP;
 #pragma unroll
@@ -126,16 +127,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
       const u32x4* vp = reinterpret_cast<const u32x4*>(p.vc + off);
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
-        kr[buf][pass][c] = kp[c];
-        vr[buf][pass][c] = vp[c];
+        rk[pass][c] = kp[c];
+        rv[pass][c] = vp[c];
       }
     }
   };
 
-  if (blk_first < blk_last) fetch(blk_first, 0);
+  if (blk_first < blk_last) fetch(blk_first, ck, cv);
   for (int i = blk_first; i < blk_last; ++i) {
-    const int buf = (i - blk_first) & 1;
-    if (i + 1 < blk_last) fetch(i + 1, buf ^ 1);
+    if (i + 1 < blk_last) fetch(i + 1, nk, nv);
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
       const int t = s_tok + i * kBlock + pass * 8 + tok;
@@ -148,9 +148,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
         for (int c = 0; c < NV; ++c)
 #pragma unroll
           for (int w = 0; w < 4; ++w)
-            s = __builtin_amdgcn_fdot2_f32_bf16(
-                __builtin_bit_cast(bf16x2, qv[h][4 * c + w]),
-                __builtin_bit_cast(bf16x2, kr[buf][pass][c][w]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[h][4 * c + w]),
+                                                as_bf16x2(ck[pass][c][w]), s, false);
         s += dpp_f32<kDppXor1>(s);
         s += dpp_f32<kDppXor2>(s);
         s += dpp_f32<kDppHalfMirror>(s);
@@ -175,7 +174,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
       for (int c = 0; c < NV; ++c)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t u = valid ? vr[buf][pass][c][w] : 0u;  // tail slots may hold NaN
+          const uint32_t u = valid ? cv[pass][c][w] : 0u;  // tail slots may hold NaN
           vf[8 * c + 2 * w] = bf16lo_to_f32(u);
           vf[8 * c + 2 * w + 1] = bf16hi_to_f32(u);
         }
@@ -187,6 +186,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
         for (int j = 0; j < DP; ++j) acc[h][j] += pr * vf[j];
       }
     }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        ck[pass][c] = nk[pass][c];
+        cv[pass][c] = nv[pass][c];
+      }
   }
 
   // merge the 8 token slots (lanes differing in bits 3..5) at a common max

@@ -14,7 +14,8 @@
 //     layout lane l holds column l % 32, i.e. one query row, and 16 keys, so
 //     the row max / row sum are in-lane plus one exchange with lane l ^ 32.
 //   * O^T = V^T P^T, again 32x32x16: B = P^T straight from the score
-//     registers (converted to bf16, round-to-nearest-even), A = V^T read from
+//     registers (converted to bf16, round-to-nearest-even; the row sum is
+//     taken over the float32 values, so LSE is exact to fp32), A = V^T read from
 //     an LDS copy of V stored transposed (keys contiguous per feature).  The
 //     key order inside each 16-key chunk is permuted so that every lane's 8
 //     keys of P match one 16-byte LDS read of V^T; the contraction does not
@@ -37,23 +38,30 @@ constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;  // query rows per work group
 constexpr int kThreads = kWaves * 64;
+constexpr float kLazy = 8.0f;  // rescale only when a row max grows by more than 2^8
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D>
 struct Tile {
-  static constexpr int BN = (D == 128) ? 64 : 128;  // keys per tile
+  static constexpr int BN = 64;                      // keys per tile
   static constexpr int NKB = BN / 32;                // 32-key blocks of S^T
   static constexpr int NDB = D / 32;                 // 32-feature blocks of O^T
   static constexpr int KC = D / 16;                  // k-chunks of K Q^T
   static constexpr int VC = BN / 16;                 // k-chunks of V^T P^T
-  static constexpr int KSTRIDE = D + 8;              // bf16 per K row in LDS
-  static constexpr int VSTRIDE = BN + 8;             // bf16 per V^T row in LDS
+  // Row strides in LDS (bf16 elements).  K rows are read 16 bytes per lane
+  // down 16 consecutive rows: a stride of 16*odd bytes spreads them over all
+  // banks.  V rows are read with the transposing LDS load, 4 rows x 64 bytes
+  // per half wave: a stride of 64 or 192 bytes past a multiple of 256 does.
+  static constexpr int KSTRIDE = D + 8;
+  static constexpr int VSTRIDE = D + 32;
   static constexpr int K_ELEMS = BN * KSTRIDE;
-  static constexpr int V_ELEMS = D * VSTRIDE;
+  static constexpr int V_ELEMS = BN * VSTRIDE;
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int K_CHUNKS = BN * D / 8 / kThreads;  // 16-byte K pieces per thread
-  static constexpr int V_ITEMS = BN * D / 32 / kThreads;  // (4 keys x 8 features) per thread
-  static_assert(K_CHUNKS * kThreads * 8 == BN * D, "K staging must cover the tile");
-  static_assert(V_ITEMS * kThreads * 32 == BN * D, "V staging must cover the tile");
+  static constexpr int CHUNKS = BN * D / 8 / kThreads;  // 16-byte pieces per thread, each of K and V
+  static_assert(CHUNKS * kThreads * 8 == BN * D, "staging must cover the tile");
+  static_assert((VSTRIDE * 2) % 128 == 64, "V rows must fall 64 bytes apart modulo 128");
 };
 
 struct Params {
@@ -66,16 +74,9 @@ struct Params {
   float sl2;  // scale * log2(e): scores are kept in the base-2 domain
 };
 
-// Position of key `key16` (0..15) of a 16-key chunk inside the transposed V
-// tile.  Key a*8 + g*4 + e goes to g*8 + a*4 + e: lane group g of the P^T
-// operand holds exactly keys {g*4 .. g*4+3, 8+g*4 .. 8+g*4+3} of each chunk.
-__device__ __forceinline__ int vt_pos(int key) {
-  const int chunk = key >> 4, k16 = key & 15;
-  const int a = k16 >> 3, gg = (k16 >> 2) & 1, e = k16 & 3;
-  return chunk * 16 + gg * 8 + a * 4 + e;
-}
-
-template <int D>
+// POS_SCALE: scale > 0, so the row maximum of scale*s is scale * max(s) and the
+// scaling folds into the exponent's FMA.  Otherwise every score is scaled first.
+template <int D, bool POS_SCALE>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
@@ -107,81 +108,54 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
   const int64_t q_row = (int64_t)p.Hq * D;
   bf16x8 qf[T::KC];
   {
-    const int row = qw0 + n;
-    if (row < p.Nq) {
-      const uint16_t* qp = p.q + ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D + g * 8;
+    const int row = min(qw0 + n, p.Nq - 1);  // rows past the end compute garbage, never stored
+    const uint16_t* qp = p.q + ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D + g * 8;
 #pragma unroll
-      for (int c = 0; c < T::KC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + c * 16);
-    } else {
-#pragma unroll
-      for (int c = 0; c < T::KC; ++c) qf[c] = bf16x8{};
-    }
+    for (int c = 0; c < T::KC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + c * 16);
   }
 
   const int64_t kv_row = (int64_t)p.Hkv * D;
   const uint16_t* kbase = p.k + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
   const uint16_t* vbase = p.v + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
 
-  u32x4 kreg[T::K_CHUNKS];
-  u32x4 vreg[4 * T::V_ITEMS];
-
+  // Staging: piece c of this thread is row (tid + c*256) / (D/8) of the tile,
+  // 16-byte column (tid % (D/8)).  Rows past the last key re-read the last
+  // key: their scores are masked and their probabilities are exactly zero, so
+  // a finite duplicate contributes nothing and no load needs a branch.
+  u32x4 kreg[T::CHUNKS], vreg[T::CHUNKS];
+  const int col8 = tid % (D / 8);
+  const int row0 = tid / (D / 8);
+  constexpr int kRowStep = kThreads / (D / 8);
   auto load_tile = [&](int t) {
     const int j0 = t * T::BN;
 #pragma unroll
-    for (int c = 0; c < T::K_CHUNKS; ++c) {
-      const int cid = tid + c * kThreads;
-      const int row = cid / (D / 8);
-      const int col = cid % (D / 8);
-      const int j = j0 + row;
-      kreg[c] = (j < p.Nk) ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * kv_row + col * 8)
-                           : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < T::V_ITEMS; ++i) {
-      const int it = tid + i * kThreads;
-      const int dc = it % (D / 8);
-      const int kg = it / (D / 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + kg * 4 + e;
-        vreg[i * 4 + e] = (j < p.Nk)
-            ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * kv_row + dc * 8)
-            : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int c = 0; c < T::CHUNKS; ++c) {
+      const int j = min(j0 + row0 + c * kRowStep, p.Nk - 1);
+      const int64_t off = (int64_t)j * kv_row + col8 * 8;
+      kreg[c] = *reinterpret_cast<const u32x4*>(kbase + off);
+      vreg[c] = *reinterpret_cast<const u32x4*>(vbase + off);
     }
   };
-
   auto store_tile = [&](int buf) {
     uint16_t* ks = smem + buf * T::STAGE;
     uint16_t* vs = ks + T::K_ELEMS;
 #pragma unroll
-    for (int c = 0; c < T::K_CHUNKS; ++c) {
-      const int cid = tid + c * kThreads;
-      const int row = cid / (D / 8);
-      const int col = cid % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + row * T::KSTRIDE + col * 8) = kreg[c];
-    }
-#pragma unroll
-    for (int i = 0; i < T::V_ITEMS; ++i) {
-      const int it = tid + i * kThreads;
-      const int dc = it % (D / 8);
-      const int kg = it / (D / 8);
-      const int pos = vt_pos(kg * 4);
-      const u32x4 v0 = vreg[i * 4 + 0], v1 = vreg[i * 4 + 1];
-      const u32x4 v2 = vreg[i * 4 + 2], v3 = vreg[i * 4 + 3];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // features 2w (low halves) and 2w+1 (high halves) of the 4 keys
-        u32x2 lo, hi;
-        lo[0] = (v0[w] & 0xffffu) | (v1[w] << 16);
-        lo[1] = (v2[w] & 0xffffu) | (v3[w] << 16);
-        hi[0] = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
-        hi[1] = (v2[w] >> 16) | (v3[w] & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(vs + (dc * 8 + 2 * w) * T::VSTRIDE + pos) = lo;
-        *reinterpret_cast<u32x2*>(vs + (dc * 8 + 2 * w + 1) * T::VSTRIDE + pos) = hi;
-      }
+    for (int c = 0; c < T::CHUNKS; ++c) {
+      const int row = row0 + c * kRowStep;
+      *reinterpret_cast<u32x4*>(ks + row * T::KSTRIDE + col8 * 8) = kreg[c];
+      *reinterpret_cast<u32x4*>(vs + row * T::VSTRIDE + col8 * 8) = vreg[c];
     }
   };
+
+  // Transposed V reads: for MFMA k-chunk kc and feature block db, lane
+  // (group G = lane/16, s = lane%16) points at key kc*16 + (G/2)*4 + s/4
+  // (+8 for the second read) and features db*32 + 16*(G%2) + 4*(s%4).  The
+  // hardware hands lane 4r+c of each 16-lane group the 4 keys of source lanes
+  // r, r+4, r+8, r+12 at feature 4r+c, which is V^T in the operand layout, with
+  // lane group g holding keys {g*4..g*4+3, 8+g*4..8+g*4+3} of the chunk.
+  const int G16 = lane >> 4, s16 = lane & 15;
+  const int vt_key = (G16 >> 1) * 4 + (s16 >> 2);
+  const int vt_col = 16 * (G16 & 1) + 4 * (s16 & 3);
 
   float m_run = kNegInf;  // running row max (base-2 domain), same in lanes n and n+32
   float l_run = 0.f;      // running row sum over this lane's keys
@@ -222,14 +196,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
         }
       }
 
-      // scale into the base-2 domain; mask only tiles that cut the band or the tail
+      if (!POS_SCALE) {
+#pragma unroll
+        for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st[kb][r] *= p.sl2;
+      }
+      // mask only tiles that cut the causal/window band or the key tail
       const bool need_mask = (j0 + T::BN > p.Nk) ||
                              (p.causal && j0 + T::BN - 1 > qw0 + delta) ||
                              (p.window > 0 && qw0 + kRowsPerWave - 1 + delta - j0 >= p.window);
-#pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[kb][r] *= p.sl2;
       if (need_mask) {
         const int pos = qw0 + n + delta;
 #pragma unroll
@@ -244,17 +220,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
           }
       }
 
-      // online softmax update
+      // online softmax with a lazily raised maximum: the stored max only moves
+      // when some row's max exceeds it by more than 2^8, so most tiles skip
+      // the accumulator rescale; probabilities stay <= 2^8, and the final
+      // division uses the sum taken at the same max, so the result is exact.
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
       mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // row with nothing visible yet
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
+      if (POS_SCALE) mx *= p.sl2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;  // row with nothing visible yet
 
       uint32_t pk[T::NKB][8];
       float rs = 0.f;
@@ -262,17 +249,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
       for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float p0 = fast_exp2(st[kb][2 * i] - m_use);
-          const float p1 = fast_exp2(st[kb][2 * i + 1] - m_use);
-          const uint32_t w = pack_bf16x2(p0, p1);
-          pk[kb][i] = w;
-          rs += bf16lo_to_f32(w) + bf16hi_to_f32(w);  // the sum of what the MFMA sees
+          float p0, p1;
+          if (POS_SCALE) {
+            p0 = fast_exp2(fmaf(st[kb][2 * i], p.sl2, -m_use));
+            p1 = fast_exp2(fmaf(st[kb][2 * i + 1], p.sl2, -m_use));
+          } else {
+            p0 = fast_exp2(st[kb][2 * i] - m_use);
+            p1 = fast_exp2(st[kb][2 * i + 1] - m_use);
+          }
+          pk[kb][i] = pack_bf16x2(p0, p1);
+          rs += p0 + p1;  // float32 sum: the LSE must reproduce exp(S - LSE) to fp32
         }
-      l_run = l_run * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      l_run += rs;
 
       // O^T += V^T P^T
 #pragma unroll
@@ -284,10 +272,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
         pw[2] = pk[kb][half * 4 + 2];
         pw[3] = pk[kb][half * 4 + 3];
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+        const uint16_t* vrow = vs + (kc * 16 + vt_key) * T::VSTRIDE + vt_col;
 #pragma unroll
         for (int db = 0; db < T::NDB; ++db) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vrow + db * 32));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vrow + 8 * T::VSTRIDE + db * 32));
           const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(vs + (db * 32 + n) * T::VSTRIDE + kc * 16 + g * 8);
+              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, acc[db], 0, 0, 0);
         }
       }
@@ -344,10 +337,18 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.sl2 = a.scale * kLog2e;
   if (p.total == 0) return hipSuccess;
   const dim3 grid(p.total), block(kThreads);
-  if (a.d == 128)
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, stream, p);
+  const bool pos = a.scale > 0.f;
+  if (a.d == 128) {
+    if (pos)
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, p);
+  } else {
+    if (pos)
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 
