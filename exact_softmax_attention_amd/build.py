@@ -67,7 +67,8 @@ def _compile(src: str):
                                         "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+        errs = "\n".join(ln for ln in res.stderr.splitlines() if "remark:" not in ln)
+        raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{res.stdout}{errs}")
     usage = _resources(res.stderr)
     # A kernel that spills or keeps arrays in scratch memory is a build error:
     # it is always a performance bug in these kernels.

@@ -9,18 +9,19 @@
 // add).
 //
 // Kernel 1 (split): one wave per (sequence, KV head, group of GH query heads,
-// 256-token split).  Lane l = (token slot l / 8, feature slice l % 8): each
-// lane loads D/8 features of one token's K and V row (16 or 32 contiguous
-// bytes; the 8 slices of a token cover its 256-byte row), so a pass covers 8
-// tokens and a 16-token block takes two passes.  Scores: v_dot2_f32_bf16 on
-// the bf16 pairs of q and k, then an all-reduce over the 8 slices with DPP.
+// 256-token split).  Lane l = (token slot l / (D/8), feature slice l % (D/8)):
+// each lane loads 8 features (16 contiguous bytes) of one token's K and V
+// row, so a pass covers 64/(D/8) tokens and a 16-token block takes 4 passes
+// (D = 128) or 2 (D = 64).  Scores: v_dot2_f32_bf16 on the bf16 pairs of q and
+// k, then an all-reduce over the D/8 slices with DPP.
 // Each lane keeps its own running max per head and only rescales when some
 // lane's score exceeds its max by more than 2^8 (wave-uniform branch), which
 // is exact algebra: the final merge divides by a sum taken at the same max.
 // P V is accumulated in float32 on the lane's own feature slice.  At the end
-// the 8 token slots are merged (same rule) and one partial per query head is
+// the token slots are merged (same rule) and one partial per query head is
 // written to the workspace.  The next block's K/V loads are issued before the
-// current block is computed.
+// current block is computed; the small per-lane state lets two waves share a
+// SIMD, which keeps enough loads in flight for the HBM bandwidth.
 //
 // Kernel 2 (combine): one work group per (sequence, query head); 4 waves each
 // take every 4th split, rescale to the common maximum and sum in a fixed
@@ -57,14 +58,15 @@ __device__ __forceinline__ int split_lo_token(int L, int window) {
 
 template <int GH, int D>
 __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
-  constexpr int DP = D / 8;   // features per lane
-  constexpr int DW = DP / 2;  // dwords per lane per row
-  constexpr int NV = DW / 4;  // 16-byte loads per lane per row
-  static_assert(NV * 4 == DW, "slice must be a whole number of 16-byte loads");
+  constexpr int DP = 8;            // features per lane: one 16-byte piece of a row
+  constexpr int PARTS = D / DP;    // lanes sharing one token row (16 or 8)
+  constexpr int TPP = 64 / PARTS;  // tokens per pass (4 or 8)
+  constexpr int PASSES = kBlock / TPP;
+  static_assert(PARTS == 8 || PARTS == 16, "head dimension 64 or 128");
 
   const int lane = threadIdx.x;
-  const int tok = lane >> 3;
-  const int part = lane & 7;
+  const int tok = lane / PARTS;
+  const int part = lane % PARTS;
   const int split = blockIdx.x;
   const int hk = blockIdx.y / p.hgroups;
   const int h0 = hk * p.group + (blockIdx.y % p.hgroups) * GH;
@@ -76,19 +78,45 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
   const int s_tok = split * kSplit;
   if (s_tok >= L || s_tok + kSplit <= lo) return;  // no visible token here
 
-  uint32_t qv[GH][DW];
+  // blocks of this split that hold visible tokens
+  const int blk_first = max(s_tok, lo) / kBlock - split * kSplitBlocks;
+  const int blk_last = min(kSplitBlocks, (L - s_tok + kBlock - 1) / kBlock);  // exclusive
+  const int* trow = p.table + (int64_t)b * p.max_blocks + split * kSplitBlocks;
+  const int64_t row_elems = (int64_t)p.Hkv * D;  // one token's row of the pool
+  bool bad = false;
+
+  // K/V registers of one block, [pass]: `ck/cv` are being computed while the
+  // next block's loads land in `nk/nv`.  Only static indices, and no branch
+  // around the loads, so that everything stays in registers.  A block id
+  // outside the pool is replaced by block 0 (an in-bounds read) and the split
+  // is flagged, which makes the whole sequence NaN.
+  u32x4 ck[PASSES], cv[PASSES], nk[PASSES], nv[PASSES];
+  auto fetch = [&](int i, u32x4 (&rk)[PASSES], u32x4 (&rv)[PASSES]) {
+    int phys = trow[i];
+    if (phys < 0 || phys >= p.num_blocks) {
+      bad = true;
+      phys = 0;
+    }
+    const int64_t base = ((int64_t)phys * kBlock) * row_elems + (int64_t)hk * D + part * DP;
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int64_t off = base + (int64_t)(pass * TPP + tok) * row_elems;
+      rk[pass] = *reinterpret_cast<const u32x4*>(p.kc + off);
+      rv[pass] = *reinterpret_cast<const u32x4*>(p.vc + off);
+    }
+  };
+  // the first block's loads go out before the query's, so both latencies overlap
+  if (blk_first < blk_last) fetch(blk_first, ck, cv);
+
+  uint32_t qv[GH][4];
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(
-        p.q + ((int64_t)b * p.Hq + h0 + h) * D + part * DP);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const u32x4 x = qp[i];
-      qv[h][4 * i + 0] = x[0];
-      qv[h][4 * i + 1] = x[1];
-      qv[h][4 * i + 2] = x[2];
-      qv[h][4 * i + 3] = x[3];
-    }
+    const u32x4 x = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)b * p.Hq + h0 + h) * D +
+                                                    part * DP);
+    qv[h][0] = x[0];
+    qv[h][1] = x[1];
+    qv[h][2] = x[2];
+    qv[h][3] = x[3];
   }
 
   float m[GH], l[GH], acc[GH][DP];
@@ -100,59 +128,24 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
     for (int j = 0; j < DP; ++j) acc[h][j] = 0.f;
   }
 
-  // blocks of this split that hold visible tokens
-  const int blk_first = max(s_tok, lo) / kBlock - split * kSplitBlocks;
-  const int blk_last = min(kSplitBlocks, (L - s_tok + kBlock - 1) / kBlock);  // exclusive
-  const int* trow = p.table + (int64_t)b * p.max_blocks + split * kSplitBlocks;
-  const int64_t row_elems = (int64_t)p.Hkv * D;  // one token's row of the pool
-  bool bad = false;
-
-  // K/V registers of one block, [pass][piece]: `ck/cv` are being computed
-  // while the next block's loads land in `nk/nv`.  Only static indices, and no
-  // branch around the loads, so that everything stays in registers.  A block
-  // id outside the pool is replaced by block 0 (an in-bounds read) and the
-  // split is flagged, which makes the whole sequence NaN.
-  u32x4 ck[2][NV], cv[2][NV], nk[2][NV], nv[2][NV];
-  auto fetch = [&](int i, u32x4 (&rk)[2][NV], u32x4 (&rv)[2][NV]) {
-    int phys = trow[i];
-    if (phys < 0 || phys >= p.num_blocks) {
-      bad = true;
-      phys = 0;
-    }
-    const int64_t base = ((int64_t)phys * kBlock) * row_elems + (int64_t)hk * D + part * DP;
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int64_t off = base + (int64_t)(pass * 8 + tok) * row_elems;
-      const u32x4* kp = reinterpret_cast<const u32x4*>(p.kc + off);
-      const u32x4* vp = reinterpret_cast<const u32x4*>(p.vc + off);
-#pragma unroll
-      for (int c = 0; c < NV; ++c) {
-        rk[pass][c] = kp[c];
-        rv[pass][c] = vp[c];
-      }
-    }
-  };
-
-  if (blk_first < blk_last) fetch(blk_first, ck, cv);
   for (int i = blk_first; i < blk_last; ++i) {
     if (i + 1 < blk_last) fetch(i + 1, nk, nv);
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int t = s_tok + i * kBlock + pass * 8 + tok;
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int t = s_tok + i * kBlock + pass * TPP + tok;
       const bool valid = t < L && t >= lo;
       float x[GH];
 #pragma unroll
       for (int h = 0; h < GH; ++h) {
         float s = 0.f;
 #pragma unroll
-        for (int c = 0; c < NV; ++c)
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[h][4 * c + w]),
-                                                as_bf16x2(ck[pass][c][w]), s, false);
+        for (int w = 0; w < 4; ++w)
+          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[h][w]), as_bf16x2(ck[pass][w]), s, false);
+        // all-reduce over the PARTS lanes of this token row
         s += dpp_f32<kDppXor1>(s);
         s += dpp_f32<kDppXor2>(s);
         s += dpp_f32<kDppHalfMirror>(s);
+        if (PARTS == 16) s += dpp_f32<kDppRor8>(s);
         x[h] = valid ? s * p.sl2 : kNegInf;
       }
       bool need = false;
@@ -171,13 +164,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
       }
       float vf[DP];
 #pragma unroll
-      for (int c = 0; c < NV; ++c)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t u = valid ? cv[pass][c][w] : 0u;  // tail slots may hold NaN
-          vf[8 * c + 2 * w] = bf16lo_to_f32(u);
-          vf[8 * c + 2 * w + 1] = bf16hi_to_f32(u);
-        }
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t u = valid ? cv[pass][w] : 0u;  // tail slots may hold NaN
+        vf[2 * w] = bf16lo_to_f32(u);
+        vf[2 * w + 1] = bf16hi_to_f32(u);
+      }
 #pragma unroll
       for (int h = 0; h < GH; ++h) {
         const float pr = (x[h] == kNegInf) ? 0.f : fast_exp2(x[h] - m[h]);
@@ -187,32 +178,28 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
       }
     }
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass)
-#pragma unroll
-      for (int c = 0; c < NV; ++c) {
-        ck[pass][c] = nk[pass][c];
-        cv[pass][c] = nv[pass][c];
-      }
+    for (int pass = 0; pass < PASSES; ++pass) {
+      ck[pass] = nk[pass];
+      cv[pass] = nv[pass];
+    }
   }
 
-  // merge the 8 token slots (lanes differing in bits 3..5) at a common max
+  // merge the TPP token slots (lanes differing in the bits above PARTS) at a
+  // common max
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
     float M = m[h];
-    M = fmaxf(M, __shfl_xor(M, 8, 64));
-    M = fmaxf(M, __shfl_xor(M, 16, 64));
-    M = fmaxf(M, __shfl_xor(M, 32, 64));
+#pragma unroll
+    for (int o = PARTS; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     const float f = (m[h] == kNegInf) ? 0.f : fast_exp2(m[h] - M);
     float ls = l[h] * f;
-    ls += __shfl_xor(ls, 8, 64);
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
+#pragma unroll
+    for (int o = PARTS; o < 64; o <<= 1) ls += __shfl_xor(ls, o, 64);
 #pragma unroll
     for (int j = 0; j < DP; ++j) {
       float a = acc[h][j] * f;
-      a += __shfl_xor(a, 8, 64);
-      a += __shfl_xor(a, 16, 64);
-      a += __shfl_xor(a, 32, 64);
+#pragma unroll
+      for (int o = PARTS; o < 64; o <<= 1) a += __shfl_xor(a, o, 64);
       acc[h][j] = a;
     }
     m[h] = M;
@@ -224,15 +211,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
     for (int h = 0; h < GH; ++h) {
       const int64_t slot = ((int64_t)b * p.Hq + h0 + h) * p.max_splits + split;
       float* dst = p.ws_acc + slot * D + part * DP;
-#pragma unroll
-      for (int j = 0; j < DP; j += 4) {
-        f32x4 w;
-        w[0] = acc[h][j];
-        w[1] = acc[h][j + 1];
-        w[2] = acc[h][j + 2];
-        w[3] = acc[h][j + 3];
-        *reinterpret_cast<f32x4*>(dst + j) = w;
-      }
+      f32x4 w0, w1;
+      w0[0] = acc[h][0]; w0[1] = acc[h][1]; w0[2] = acc[h][2]; w0[3] = acc[h][3];
+      w1[0] = acc[h][4]; w1[1] = acc[h][5]; w1[2] = acc[h][6]; w1[3] = acc[h][7];
+      reinterpret_cast<f32x4*>(dst)[0] = w0;
+      reinterpret_cast<f32x4*>(dst)[1] = w1;
       if (part == 0)
         p.ws_ml[slot] = any_bad ? make_float2(__builtin_nanf(""), __builtin_nanf(""))
                                 : make_float2(m[h], l[h]);

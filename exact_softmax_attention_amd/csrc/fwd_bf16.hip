@@ -8,23 +8,30 @@
 // for a backward pass.  Score and probability tiles live only in registers.
 //
 // MI355X mapping (this library's own design):
-//   * 4 waves x 32 query rows = 128 rows per work group.  Each wave computes
-//     S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = its
-//     Q rows held in registers for the whole loop).  In the 32x32 accumulator
-//     layout lane l holds column l % 32, i.e. one query row, and 16 keys, so
-//     the row max / row sum are in-lane plus one exchange with lane l ^ 32.
+//   * 8 waves x 32 query rows = 256 rows per work group, one work group per
+//     CU, so each SIMD runs two waves.  Each wave computes S^T = K Q^T with
+//     v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = its Q rows held in
+//     registers for the whole loop).  In the 32x32 accumulator layout lane l
+//     holds column l % 32, i.e. one query row, and 16 keys, so the row max /
+//     row sum are in-lane plus one exchange with lane l ^ 32.
 //   * O^T = V^T P^T, again 32x32x16: B = P^T straight from the score
 //     registers (converted to bf16, round-to-nearest-even; the row sum is
-//     taken over the float32 values, so LSE is exact to fp32), A = V^T read from
-//     an LDS copy of V stored transposed (keys contiguous per feature).  The
-//     key order inside each 16-key chunk is permuted so that every lane's 8
-//     keys of P match one 16-byte LDS read of V^T; the contraction does not
-//     care about the order as long as both operands agree.
-//   * K/V tiles are staged global -> registers -> LDS with two LDS buffers:
-//     the next tile's global loads are in flight while the current tile is
-//     computed.  Tiles wholly outside the causal/window band are never
-//     visited; only tiles that cut the band boundary or the key tail pay for
-//     the per-element mask.
+//     taken over the float32 values, so LSE is exact to fp32), A = V^T read
+//     with the LDS transpose load (ds_read_b64_tr_b16) from a row-major V
+//     tile.  The MFMA k index is a permutation of the tile's keys, the same
+//     for both operands.
+//   * The two waves of a SIMD are kept in opposite phases ("ping-pong"): while
+//     one issues the matrix products, the other computes its softmax on the
+//     vector ALUs; a workgroup barrier swaps the phases (see the schedule
+//     comment at the kernel).
+//   * K/V tiles are staged global -> registers -> LDS (two slots per kind),
+//     group A moving K and group B moving V during their vector phases; LDS
+//     rows are padded so that the fragment reads are bank-conflict free, and
+//     fragment reads run several MFMAs ahead of their use.
+//   * Tiles wholly outside the causal/window band are never visited; only
+//     tiles that cut the band boundary or the key tail pay for the per-element
+//     mask.  The row maximum is raised lazily (only when a row's max grows by
+//     more than 2^8), so most tiles skip the accumulator rescale.
 //   * Work groups are ordered heavy-first (last query tiles first) inside a
 //     head and remapped so that the tiles of one head share an XCD (and its
 //     L2), since they all stream the same K/V.
@@ -34,10 +41,11 @@
 namespace attn {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                    // two groups of 4, one wave of each per SIMD
 constexpr int kRowsPerWave = 32;
-constexpr int kBM = kWaves * kRowsPerWave;  // query rows per work group
+constexpr int kBM = kWaves * kRowsPerWave;   // query rows per work group
 constexpr int kThreads = kWaves * 64;
+constexpr int kGroupThreads = kThreads / 2;
 constexpr float kLazy = 8.0f;  // rescale only when a row max grows by more than 2^8
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -58,9 +66,8 @@ struct Tile {
   static constexpr int VSTRIDE = D + 32;
   static constexpr int K_ELEMS = BN * KSTRIDE;
   static constexpr int V_ELEMS = BN * VSTRIDE;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int CHUNKS = BN * D / 8 / kThreads;  // 16-byte pieces per thread, each of K and V
-  static_assert(CHUNKS * kThreads * 8 == BN * D, "staging must cover the tile");
+  static constexpr int CHUNKS = BN * D / 8 / kGroupThreads;  // 16-byte pieces per group thread
+  static_assert(CHUNKS * kGroupThreads * 8 == BN * D, "staging must cover the tile");
   static_assert((VSTRIDE * 2) % 128 == 64, "V rows must fall 64 bytes apart modulo 128");
 };
 
@@ -74,16 +81,32 @@ struct Params {
   float sl2;  // scale * log2(e): scores are kept in the base-2 domain
 };
 
+// Schedule ("ping-pong").  The 8 waves form two groups, A = waves 0-3 and
+// B = waves 4-7, so each SIMD runs one wave of each.  Every wave alternates
+// an MFMA phase, M(k) = scores of tile k and P V of tile k-1, with a vector
+// phase, V(k) = softmax of tile k.  Group B runs one barrier behind group A,
+// so while one group keeps the matrix cores busy the other does its softmax;
+// the phases swap at every barrier.  Barrier slots: A does M(k) in slot 2k
+// and V(k) in 2k+1; B does M(k) in 2k+1 and V(k) in 2k+2.
+//
+// Staging (two K and two V slots in LDS): A, in V(k), stores K(k+1) and
+// starts loading K(k+2); B, in V(k), stores V(k+1) and starts loading V(k+2).
+// K(k+1) lands in the slot of K(k-1), last read in slot 2k-1, and is first
+// read in slot 2k+2; V(k+1) lands in the slot of V(k-1), last read in slot
+// 2k+1, and is first read in slot 2k+4.
+//
 // POS_SCALE: scale > 0, so the row maximum of scale*s is scale * max(s) and the
 // scaling folds into the exponent's FMA.  Otherwise every score is scaled first.
 template <int D, bool POS_SCALE>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (T::K_ELEMS + T::V_ELEMS)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const bool group_b = wave >= kWaves / 2;
+  const int gtid = tid & (kGroupThreads - 1);
   const int n = lane & 31;  // query row within the wave / MFMA column
   const int g = lane >> 5;  // k-half of the MFMA operands
 
@@ -102,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
   int kv_begin = 0;
   if (p.window > 0) kv_begin = max(0, i0 + delta - p.window + 1);
   const int t_begin = kv_begin / T::BN;
-  const int t_end = kv_end > kv_begin ? (kv_end + T::BN - 1) / T::BN : t_begin;
+  const int n_tiles = kv_end > kv_begin ? (kv_end + T::BN - 1) / T::BN - t_begin : 0;
 
   // this wave's Q rows as the B operand of K Q^T (8 bf16 per k-chunk)
   const int64_t q_row = (int64_t)p.Hq * D;
@@ -114,37 +137,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
     for (int c = 0; c < T::KC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + c * 16);
   }
 
+  // Staging: group A moves K tiles, group B V tiles.  Piece c of a group
+  // thread is row (gtid + c*256) / (D/8) of the tile, 16-byte column
+  // gtid % (D/8).  Rows past the last key re-read the last key: their scores
+  // are masked and their probabilities are exactly zero, so a finite duplicate
+  // contributes nothing.
   const int64_t kv_row = (int64_t)p.Hkv * D;
-  const uint16_t* kbase = p.k + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
-  const uint16_t* vbase = p.v + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
-
-  // Staging: piece c of this thread is row (tid + c*256) / (D/8) of the tile,
-  // 16-byte column (tid % (D/8)).  Rows past the last key re-read the last
-  // key: their scores are masked and their probabilities are exactly zero, so
-  // a finite duplicate contributes nothing and no load needs a branch.
-  u32x4 kreg[T::CHUNKS], vreg[T::CHUNKS];
-  const int col8 = tid % (D / 8);
-  const int row0 = tid / (D / 8);
-  constexpr int kRowStep = kThreads / (D / 8);
-  auto load_tile = [&](int t) {
-    const int j0 = t * T::BN;
+  const uint16_t* src = (group_b ? p.v : p.k) + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
+  const int col8 = gtid % (D / 8);
+  const int row0 = gtid / (D / 8);
+  constexpr int kRowStep = kGroupThreads / (D / 8);
+  const int dst_stride = group_b ? T::VSTRIDE : T::KSTRIDE;
+  u32x4 sreg[T::CHUNKS];
+  auto kslot = [&](int i) { return smem + (i & 1) * T::K_ELEMS; };
+  auto vslot = [&](int i) { return smem + 2 * T::K_ELEMS + (i & 1) * T::V_ELEMS; };
+  auto stage_load = [&](int k) {  // tile index k relative to t_begin
+    const int j0 = (t_begin + k) * T::BN;
 #pragma unroll
     for (int c = 0; c < T::CHUNKS; ++c) {
       const int j = min(j0 + row0 + c * kRowStep, p.Nk - 1);
-      const int64_t off = (int64_t)j * kv_row + col8 * 8;
-      kreg[c] = *reinterpret_cast<const u32x4*>(kbase + off);
-      vreg[c] = *reinterpret_cast<const u32x4*>(vbase + off);
+      sreg[c] = *reinterpret_cast<const u32x4*>(src + (int64_t)j * kv_row + col8 * 8);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * T::STAGE;
-    uint16_t* vs = ks + T::K_ELEMS;
+  auto stage_store = [&](int k) {
+    uint16_t* dst = group_b ? vslot(k) : kslot(k);
 #pragma unroll
-    for (int c = 0; c < T::CHUNKS; ++c) {
-      const int row = row0 + c * kRowStep;
-      *reinterpret_cast<u32x4*>(ks + row * T::KSTRIDE + col8 * 8) = kreg[c];
-      *reinterpret_cast<u32x4*>(vs + row * T::VSTRIDE + col8 * 8) = vreg[c];
-    }
+    for (int c = 0; c < T::CHUNKS; ++c)
+      *reinterpret_cast<u32x4*>(dst + (row0 + c * kRowStep) * dst_stride + col8 * 8) = sreg[c];
   };
 
   // Transposed V reads: for MFMA k-chunk kc and feature block db, lane
@@ -157,52 +176,97 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
   const int vt_key = (G16 >> 1) * 4 + (s16 >> 2);
   const int vt_col = 16 * (G16 & 1) + 4 * (s16 & 3);
 
+  auto wave_skips = [&](int k) {
+    const int j0 = (t_begin + k) * T::BN;
+    bool skip = qw0 >= p.Nq;
+    if (p.causal && j0 > qw0 + kRowsPerWave - 1 + delta) skip = true;
+    if (p.window > 0 && j0 + T::BN - 1 < qw0 + delta - p.window + 1) skip = true;
+    return skip;
+  };
+
   float m_run = kNegInf;  // running row max (base-2 domain), same in lanes n and n+32
   float l_run = 0.f;      // running row sum over this lane's keys
   f32x16 acc[T::NDB];
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) acc[db] = f32x16{};
+  f32x16 st[T::NKB];          // scores of the tile between its M and V phases
+  uint32_t pk[T::NKB][8];     // bf16 probabilities between a V phase and the next M phase
 
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bool has_next = t + 1 < t_end;
-    if (has_next) load_tile(t + 1);
-    const int j0 = t * T::BN;
-
-    bool skip = qw0 >= p.Nq;
-    if (p.causal && j0 > qw0 + kRowsPerWave - 1 + delta) skip = true;
-    if (p.window > 0 && j0 + T::BN - 1 < qw0 + delta - p.window + 1) skip = true;
-
-    if (!skip) {
-      const uint16_t* ks = smem + buf * T::STAGE;
-      const uint16_t* vs = ks + T::K_ELEMS;
-
-      // S^T = K Q^T for the tile's NKB blocks of 32 keys
-      f32x16 st[T::NKB];
+  // M(k): scores of tile k, then P V of tile k-1.  The fragment reads run a
+  // few MFMAs ahead of their use so that the LDS latency stays hidden.
+  auto m_phase = [&](int k) {
+    __builtin_amdgcn_s_setprio(1);
+    if (k < n_tiles && !wave_skips(k)) {
+      const uint16_t* ks = kslot(k) + n * T::KSTRIDE + g * 8;
+      constexpr int NQK = T::NKB * T::KC;  // MFMAs of the score tile
+      constexpr int LA = 8;                // reads in flight ahead
+      bf16x8 kf[NQK];
 #pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb) {
-        st[kb] = f32x16{};
+      for (int i = 0; i < LA; ++i)
+        kf[i] = *reinterpret_cast<const bf16x8*>(ks + (i / T::KC) * 32 * T::KSTRIDE + (i % T::KC) * 16);
 #pragma unroll
-        for (int c = 0; c < T::KC; ++c) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + n) * T::KSTRIDE + c * 16 + g * 8);
-          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[kb], 0, 0, 0);
-        }
+      for (int kb = 0; kb < T::NKB; ++kb) st[kb] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        if (i + LA < NQK)
+          kf[i + LA] = *reinterpret_cast<const bf16x8*>(
+              ks + ((i + LA) / T::KC) * 32 * T::KSTRIDE + ((i + LA) % T::KC) * 16);
+        st[i / T::KC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i % T::KC], st[i / T::KC], 0, 0, 0);
       }
+      // keep LA reads in flight: reads, then alternate one MFMA / one read
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + LA < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    if (k >= 1 && !wave_skips(k - 1)) {
+      const uint16_t* vrow = vslot(k - 1) + vt_key * T::VSTRIDE + vt_col;
+      constexpr int NPV = T::VC * T::NDB;  // MFMAs of the P V update
+      constexpr int LA = 6;
+      bf16x8 vf[NPV];
+      auto vread = [&](int i) {  // i = kc * NDB + db
+        const uint16_t* r = vrow + (i / T::NDB) * 16 * T::VSTRIDE + (i % T::NDB) * 32;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)r);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r + 8 * T::VSTRIDE));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+#pragma unroll
+      for (int i = 0; i < LA; ++i) vf[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        if (i + LA < NPV) vf[i + LA] = vread(i + LA);
+        const int kc = i / T::NDB, db = i % T::NDB;
+        const int kb = kc >> 1, half = kc & 1;
+        u32x4 pw;
+        pw[0] = pk[kb][half * 4 + 0];
+        pw[1] = pk[kb][half * 4 + 1];
+        pw[2] = pk[kb][half * 4 + 2];
+        pw[3] = pk[kb][half * 4 + 3];
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], __builtin_bit_cast(bf16x8, pw),
+                                                         acc[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 1);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (i + LA < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
 
+  // V(k): softmax of tile k (mask, lazy max, exponentials), then staging
+  auto v_phase = [&](int k) {
+    if (k < n_tiles && !wave_skips(k)) {
+      const int j0 = (t_begin + k) * T::BN;
       if (!POS_SCALE) {
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) st[kb][r] *= p.sl2;
       }
-      // mask only tiles that cut the causal/window band or the key tail
       const bool need_mask = (j0 + T::BN > p.Nk) ||
                              (p.causal && j0 + T::BN - 1 > qw0 + delta) ||
                              (p.window > 0 && qw0 + kRowsPerWave - 1 + delta - j0 >= p.window);
@@ -219,7 +283,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
             if (!vis) st[kb][r] = kNegInf;
           }
       }
-
       // online softmax with a lazily raised maximum: the stored max only moves
       // when some row's max exceeds it by more than 2^8, so most tiles skip
       // the accumulator rescale; probabilities stay <= 2^8, and the final
@@ -242,8 +305,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
         m_run = m_new;
       }
       const float m_use = (m_run == kNegInf) ? 0.f : m_run;  // row with nothing visible yet
-
-      uint32_t pk[T::NKB][8];
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb)
@@ -261,34 +322,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const Params p) {
           rs += p0 + p1;  // float32 sum: the LSE must reproduce exp(S - LSE) to fp32
         }
       l_run += rs;
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kc = 0; kc < T::VC; ++kc) {
-        const int kb = kc >> 1, half = kc & 1;
-        u32x4 pw;
-        pw[0] = pk[kb][half * 4 + 0];
-        pw[1] = pk[kb][half * 4 + 1];
-        pw[2] = pk[kb][half * 4 + 2];
-        pw[3] = pk[kb][half * 4 + 3];
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        const uint16_t* vrow = vs + (kc * 16 + vt_key) * T::VSTRIDE + vt_col;
-#pragma unroll
-        for (int db = 0; db < T::NDB; ++db) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vrow + db * 32));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vrow + 8 * T::VSTRIDE + db * 32));
-          const bf16x8 vf =
-              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, acc[db], 0, 0, 0);
-        }
-      }
     }
+    if (k + 1 < n_tiles) stage_store(k + 1);
+    if (k + 2 < n_tiles) stage_load(k + 2);
+  };
 
-    if (has_next) store_tile(buf ^ 1);
+  // prologue: K(0) in LDS; A holds K(1), B holds V(0) in registers
+  if (n_tiles > 0) {
+    if (!group_b) {
+      stage_load(0);
+      stage_store(0);
+      if (n_tiles > 1) stage_load(1);
+    } else {
+      stage_load(0);
+    }
+  }
+  __syncthreads();
+  if (group_b) {  // B's V(-1): store V(0), start V(1)
+    if (n_tiles > 0) stage_store(0);
+    if (n_tiles > 1) stage_load(1);
     __syncthreads();
   }
+  for (int k = 0; k <= n_tiles; ++k) {
+    m_phase(k);
+    __syncthreads();
+    v_phase(k);
+    __syncthreads();
+  }
+  if (!group_b) __syncthreads();  // A's extra barrier matches B's first one
 
   // epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
   const float l_tot = l_run + swap_halves(l_run);
