@@ -13,8 +13,16 @@ Prints ONE JSON line.  `value` is the prefill throughput in TFLOP/s
 around each launch on the stream the kernels run on; the decode throughput in
 GB/s of algorithmic HBM bytes is reported beside it.  `roofline` is for the
 prefill kernel (bound: bf16 MFMA), `decode.roofline` for the decode kernels
-(bound: HBM).  `cpu_baseline` times the fp64 oracle on a bounded sample (two
-heads of the prefill workload) on the host cores and scales it to TFLOP/s.
+(bound: HBM).  `cpu_baseline` times the fp64 oracle on a bounded sample (16
+(batch, head) pairs of the prefill workload) on the host cores and scales it
+to TFLOP/s.
+
+`traffic` is the measured HBM bytes per launch, read from profiles/traffic.json
+when that file was written for the kernel sources as they are now (a hash of
+the sources is stored with it).  `--traffic-from DIR` writes that file from
+four rocprofv3 --pmc runs under DIR (fetch/, write/ of this bench, and
+copy_fetch/, copy_write/ of `--mode copy`): each counter is scaled by what it
+reads for the plain 1 GiB device copy.
 
 Other workloads can be timed with --workload NAME (one of the dense configs);
 the default line is the one described above.
@@ -68,11 +76,74 @@ def parse():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: a plain device copy of known size (counter calibration)")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="write profiles/traffic.json from rocprofv3 --pmc runs under DIR "
+                         "(no GPU needed)")
     return ap.parse_args()
 
 
-def cpu_baseline(q, k, v, cfg):
-    """Time the fp64 oracle on two heads (all rows) and scale to TFLOP/s."""
+FWD_FILES = ["fwd_bf16.hip", "device_common.h", "launch.h"]
+DECODE_FILES = ["decode_paged.hip", "device_common.h", "launch.h"]
+COPY_BYTES = 1 << 30
+
+
+def _pmc_means(path, counter):
+    """Mean counter value per dispatch, by kernel name, from a rocprofv3 counter CSV dir."""
+    import csv
+    import glob
+    sums, counts = {}, {}
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"bench: no counter_collection.csv under {path}")
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                sums[name] = sums.get(name, 0.0) + float(row["Counter_Value"])
+                counts[name] = counts.get(name, 0) + 1
+    return {n: sums[n] / counts[n] for n in sums}
+
+
+def _pick(means, key):
+    hits = [v for n, v in means.items() if key in n]
+    if len(hits) != 1:
+        raise SystemExit(f"bench: expected one kernel matching {key!r}, found {len(hits)}")
+    return hits[0]
+
+
+def write_traffic(src_dir):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch) runs.
+
+    Each counter is scaled so that it reads the true byte count for a plain
+    1 GiB device-to-device copy (the runtime's copy kernel) measured the same way.
+    """
+    fetch = _pmc_means(os.path.join(src_dir, "fetch"), "FETCH_SIZE")
+    write = _pmc_means(os.path.join(src_dir, "write"), "WRITE_SIZE")
+    cfetch = _pick(_pmc_means(os.path.join(src_dir, "copy_fetch"), "FETCH_SIZE"), "copyBuffer")
+    cwrite = _pick(_pmc_means(os.path.join(src_dir, "copy_write"), "WRITE_SIZE"), "copyBuffer")
+    f_fetch = COPY_BYTES / (cfetch * 1024.0)
+    f_write = COPY_BYTES / (cwrite * 1024.0)
+    out = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cfetch, "write_kib": cwrite,
+                           "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)}}
+    groups = {f"fwd:{PREFILL}": (["fwd_bf16_kernel"], FWD_FILES),
+              f"decode:{DECODE}": (["decode_split_kernel", "decode_combine_kernel"],
+                                   DECODE_FILES)}
+    for key, (kernels, files) in groups.items():
+        rd = sum(_pick(fetch, kn) for kn in kernels) * 1024.0 * f_fetch
+        wr = sum(_pick(write, kn) for kn in kernels) * 1024.0 * f_write
+        out[key] = {"kernels": kernels, "fetch_bytes": round(rd), "write_bytes": round(wr),
+                    "bytes_per_launch": round(rd + wr), "source_hash": kernel_source_hash(files)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+def cpu_baseline(q, k, v, cfg, n_heads=16):
+    """Time the fp64 oracle on `n_heads` (batch, head) pairs (all rows); scale to TFLOP/s."""
     import numpy as np
     import oracle
     from exact_softmax_attention_amd import metrics
@@ -82,7 +153,9 @@ def cpu_baseline(q, k, v, cfg):
                         if i.get("user_api") == "blas"), default=1)
     except Exception:  # pragma: no cover
         threads = 1
-    heads = [(0, 0), (cfg.B - 1, cfg.Hq - 1)]
+    total = cfg.B * cfg.Hq
+    step = max(1, total // n_heads)
+    heads = [divmod(i, cfg.Hq) for i in range(0, total, step)][:n_heads]
     t0 = time.perf_counter()
     oracle.attention(q, k, v, cfg.scale, cfg.causal, cfg.window, heads=heads)
     dt = time.perf_counter() - t0
@@ -118,6 +191,9 @@ def time_loop(fns, steps, warmup, torch):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU layout is described, not built", file=sys.stderr)
@@ -133,7 +209,7 @@ def main():
     dev = torch.device("cuda:0")
 
     if args.mode == "copy":
-        n = 1 << 30
+        n = COPY_BYTES
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         for _ in range(max(1, args.steps)):
@@ -184,7 +260,6 @@ def main():
     flops = metrics.fwd_flops(cfg.B, cfg.Hq, cfg.Nq, cfg.Nk, cfg.d, cfg.causal, cfg.window)
     fwd_ms = per[0]
     tflops = flops / (fwd_ms * 1e-3) / 1e12
-    fwd_files = ["fwd_bf16.hip", "device_common.h"]
     res = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -205,7 +280,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / metrics.PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(f"fwd:{name}", fwd_files),
+                     "traffic": measured_traffic(f"fwd:{name}", FWD_FILES),
                      "kernel": "fwd_bf16_kernel<128>", "ms": round(fwd_ms, 4),
                      "flop_per_launch": flops,
                      "algorithmic_bytes": metrics.fwd_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq,
@@ -225,8 +300,7 @@ def main():
                                       "peak": metrics.PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": round(gbs / metrics.PEAK_HBM_GBS, 4),
                                       "traffic": measured_traffic(f"decode:{pc.name}",
-                                                                  ["decode_paged.hip",
-                                                                   "device_common.h"]),
+                                                                  DECODE_FILES),
                                       "kernels": "decode_split_kernel<4,128> + "
                                                  "decode_combine_kernel<128>",
                                       "algorithmic_bytes": nbytes}}
