@@ -301,7 +301,7 @@ def main():
                                       "frac": round(gbs / metrics.PEAK_HBM_GBS, 4),
                                       "traffic": measured_traffic(f"decode:{pc.name}",
                                                                   DECODE_FILES),
-                                      "kernels": "decode_split_kernel<4,128> + "
+                                      "kernels": "decode_split_kernel<128> + "
                                                  "decode_combine_kernel<128>",
                                       "algorithmic_bytes": nbytes}}
     if not args.skip_cpu_baseline:

@@ -22,6 +22,10 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
 SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode_paged.hip"]
+# The decode kernel multiplies its matrix-core accumulators by the softmax
+# rescale factor on the vector ALUs every block; keeping them in ordinary
+# VGPRs (rather than AGPRs) avoids copying them back and forth.
+EXTRA_FLAGS = {"decode_paged.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 
@@ -63,7 +67,7 @@ def _resources(stderr: str):
 
 def _compile(src: str):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + ["-Rpass-analysis=kernel-resource-usage",
+    cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + ["-Rpass-analysis=kernel-resource-usage",
                                         "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

@@ -83,7 +83,9 @@ int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
     return ATTN_E_NULL;
   if (block_size != 16 || max_blocks_per_seq < 1 || num_blocks < 1) return ATTN_E_SHAPE;
   if ((long long)max_blocks_per_seq * block_size > INT_MAX) return ATTN_E_SHAPE;
-  if (B > 65535 || Hq > 65535) return ATTN_E_SHAPE;  // grid y / z limits
+  if (B > 65535 || Hq > 65535) return ATTN_E_SHAPE;  // grid y limits
+  // block counts of the whole batch are summed in 32-bit integers on the device
+  if ((long long)B * max_blocks_per_seq > INT_MAX) return ATTN_E_SHAPE;
   if (B == 0) return ATTN_OK;
   const size_t need = attn::decode_workspace_bytes(B, Hq, d, block_size, max_blocks_per_seq);
   if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;

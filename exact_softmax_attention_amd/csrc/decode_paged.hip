@@ -3,29 +3,36 @@
 // Method: a decode step's one new query reads every cached K/V of its
 // sequence ("Ch. 3: MHA Limitations, MQA, GQA, and FlashAttention", 3.1);
 // the cache is split into fixed-size blocks reached through a lookup table
-// ("Inference Engineering", 2.5); the keys are cut into splits whose partial
+// ("Inference Engineering", 2.5); the keys are cut into pieces whose partial
 // softmax states (m, l, acc) are merged exactly afterwards (the rescale of
 // "Ch. 3", 3.5: l e^m is invariant, so states rescaled to a common maximum
 // add).
 //
-// Kernel 1 (split): one wave per (sequence, KV head, group of GH query heads,
-// 256-token split).  Lane l = (token slot l / (D/8), feature slice l % (D/8)):
-// each lane loads 8 features (16 contiguous bytes) of one token's K and V
-// row, so a pass covers 64/(D/8) tokens and a 16-token block takes 4 passes
-// (D = 128) or 2 (D = 64).  Scores: v_dot2_f32_bf16 on the bf16 pairs of q and
-// k, then an all-reduce over the D/8 slices with DPP.
-// Each lane keeps its own running max per head and only rescales when some
-// lane's score exceeds its max by more than 2^8 (wave-uniform branch), which
-// is exact algebra: the final merge divides by a sum taken at the same max.
-// P V is accumulated in float32 on the lane's own feature slice.  At the end
-// the token slots are merged (same rule) and one partial per query head is
-// written to the workspace.  The next block's K/V loads are issued before the
-// current block is computed; the small per-lane state lets two waves share a
-// SIMD, which keeps enough loads in flight for the HBM bandwidth.
+// Work split.  All cache blocks the batch reads (for one KV head) are laid end
+// to end, sequence after sequence, and cut into W equal ranges, one per wave,
+// so every wave streams the same number of blocks whatever the length mix; a
+// range that crosses a sequence boundary yields one partial state per
+// sequence it touches.  A wave serves one KV head and up to 16 of the query
+// heads that share it.
+//
+// Kernel 1 (split), per 16-token block, all on the matrix cores:
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, A = 16 key rows straight from
+//                 memory (lane (n, g): token n, features 32c + 8g .. +8),
+//                 B = the query heads' rows (lane column n = head);
+//   softmax       lane (n, g) holds tokens 4g .. 4g+3 of head n: the block max
+//                 is in-lane; the running max is raised lazily (only when a
+//                 score passes it by more than 2^8), equal on a head's 4 lanes;
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16, B = the lane's own 4
+//                 probabilities (bf16, round to nearest even), A = V^T read
+//                 with the transposing LDS load from the block's V rows, which
+//                 the wave stages in its own LDS slot.
+// The next block's K/V loads are in flight while a block is computed.
 //
 // Kernel 2 (combine): one work group per (sequence, query head); 4 waves each
-// take every 4th split, rescale to the common maximum and sum in a fixed
+// take every 4th partial, rescale to the common maximum and sum in a fixed
 // order; the 4 partial sums are added in LDS.  Deterministic: no atomics.
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -33,10 +40,13 @@ namespace attn {
 namespace {
 
 constexpr int kBlock = 16;         // tokens per cache block
-constexpr int kSplit = 256;        // tokens per split
-constexpr int kSplitBlocks = kSplit / kBlock;
 constexpr float kLazy = 8.0f;      // rescale only when a score passes max + 8 (base 2)
 constexpr int kCombineWaves = 4;
+constexpr int kMaxWaves = 1024;    // waves per (KV head, head group): bounds the workspace
+constexpr int kWavesPerSimd = 2;   // resident split waves per SIMD (register bound)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct Params {
   const uint16_t* q;
@@ -46,180 +56,245 @@ struct Params {
   const int* lens;
   uint16_t* o;
   float* lse;
-  float2* ws_ml;   // [B, Hq, max_splits] (m, l)
-  float* ws_acc;   // [B, Hq, max_splits, D]
-  int Hq, Hkv, group, hgroups, max_blocks, num_blocks, window, max_splits;
+  float2* ws_ml;   // [Hq, kMaxWaves + B] (m, l); slot of (wave w, sequence b) = w + b
+  float* ws_acc;   // [Hq, kMaxWaves + B, D]
+  int2* ws_seq;    // [B] (first wave, last wave) covering the sequence
+  int B, Hq, Hkv, group, hgroups, max_blocks, num_blocks, window, W, slots;
   float sl2;
 };
 
-__device__ __forceinline__ int split_lo_token(int L, int window) {
+// Cache blocks a sequence of length L reads (0 for a length the kernels reject).
+__device__ __forceinline__ int seq_blocks(int L, int max_blocks, int window) {
+  if (L <= 0 || L > max_blocks * kBlock) return 0;
+  const int lo = window > 0 ? max(0, L - window) : 0;
+  return (L + kBlock - 1) / kBlock - lo / kBlock;
+}
+
+__device__ __forceinline__ int lo_token(int L, int window) {
   return window > 0 ? max(0, L - window) : 0;
 }
 
-template <int GH, int D>
+template <int D>
+struct DecTile {
+  static constexpr int KC = D / 32;       // 16x16x32 products over the head dimension
+  static constexpr int NT = D / 16;       // 16-feature tiles of O^T
+  static constexpr int RL = D / 8;        // lanes per token row in a V load (16 bytes each)
+  static constexpr int RPI = 64 / RL;     // token rows per V load instruction
+  static constexpr int VI = kBlock / RPI; // V load instructions per block
+  static constexpr int PITCH = D + 16;    // LDS row pitch (bf16): rows fall 32 bytes apart mod 256
+};
+
+template <int D>
 __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
-  constexpr int DP = 8;            // features per lane: one 16-byte piece of a row
-  constexpr int PARTS = D / DP;    // lanes sharing one token row (16 or 8)
-  constexpr int TPP = 64 / PARTS;  // tokens per pass (4 or 8)
-  constexpr int PASSES = kBlock / TPP;
-  static_assert(PARTS == 8 || PARTS == 16, "head dimension 64 or 128");
+  using T = DecTile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kBlock * T::PITCH];
 
   const int lane = threadIdx.x;
-  const int tok = lane / PARTS;
-  const int part = lane % PARTS;
-  const int split = blockIdx.x;
+  const int n = lane & 15;   // MFMA column: query head; also the K token row
+  const int g = lane >> 4;   // MFMA k-group
+  const int w = blockIdx.x;
   const int hk = blockIdx.y / p.hgroups;
-  const int h0 = hk * p.group + (blockIdx.y % p.hgroups) * GH;
-  const int b = blockIdx.z;
+  const int hsub = (blockIdx.y % p.hgroups) * 16;  // first head of this wave within the group
+  const int nh = min(16, p.group - hsub);          // heads this wave serves
+  const int h0 = hk * p.group + hsub;
 
-  const int L = p.lens[b];
-  if (L < 0 || L > p.max_blocks * kBlock) return;  // the combine writes NaN
-  const int lo = split_lo_token(L, p.window);
-  const int s_tok = split * kSplit;
-  if (s_tok >= L || s_tok + kSplit <= lo) return;  // no visible token here
-
-  // blocks of this split that hold visible tokens
-  const int blk_first = max(s_tok, lo) / kBlock - split * kSplitBlocks;
-  const int blk_last = min(kSplitBlocks, (L - s_tok + kBlock - 1) / kBlock);  // exclusive
-  const int* trow = p.table + (int64_t)b * p.max_blocks + split * kSplitBlocks;
-  const int64_t row_elems = (int64_t)p.Hkv * D;  // one token's row of the pool
-  bool bad = false;
-
-  // K/V registers of one block, [pass]: `ck/cv` are being computed while the
-  // next block's loads land in `nk/nv`.  Only static indices, and no branch
-  // around the loads, so that everything stays in registers.  A block id
-  // outside the pool is replaced by block 0 (an in-bounds read) and the split
-  // is flagged, which makes the whole sequence NaN.
-  u32x4 ck[PASSES], cv[PASSES], nk[PASSES], nv[PASSES];
-  auto fetch = [&](int i, u32x4 (&rk)[PASSES], u32x4 (&rv)[PASSES]) {
-    int phys = trow[i];
-    if (phys < 0 || phys >= p.num_blocks) {
-      bad = true;
-      phys = 0;
-    }
-    const int64_t base = ((int64_t)phys * kBlock) * row_elems + (int64_t)hk * D + part * DP;
+  // Blocks of all sequences laid end to end: C_b = blocks before sequence b,
+  // T = all blocks.  A wave-wide prefix sum, 64 sequences at a time, finds the
+  // total and the sequence holding this wave's first block.
+  int total = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    const int j = c + lane;
+    int x = j < p.B ? seq_blocks(p.lens[j], p.max_blocks, p.window) : 0;
 #pragma unroll
-    for (int pass = 0; pass < PASSES; ++pass) {
-      const int64_t off = base + (int64_t)(pass * TPP + tok) * row_elems;
-      rk[pass] = *reinterpret_cast<const u32x4*>(p.kc + off);
-      rv[pass] = *reinterpret_cast<const u32x4*>(p.vc + off);
-    }
-  };
-  // the first block's loads go out before the query's, so both latencies overlap
-  if (blk_first < blk_last) fetch(blk_first, ck, cv);
-
-  uint32_t qv[GH][4];
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    total += x;
+  }
+  // never more waves than blocks, so that every working wave owns at least one
+  // block and the waves covering a sequence are consecutive and all write a partial
+  const int nw = min(p.W, total);
+  if (w >= nw) return;
+  const int g0 = (int)((int64_t)w * total / nw);
+  const int g1 = (int)((int64_t)(w + 1) * total / nw);
+  int b = 0, cb = 0;  // first sequence touching [g0, g1) and its C_b
+  for (int c = 0; c < p.B; c += 64) {
+    const int j = c + lane;
+    const int x = j < p.B ? seq_blocks(p.lens[j], p.max_blocks, p.window) : 0;
+    int incl = x;
 #pragma unroll
-  for (int h = 0; h < GH; ++h) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)b * p.Hq + h0 + h) * D +
-                                                    part * DP);
-    qv[h][0] = x[0];
-    qv[h][1] = x[1];
-    qv[h][2] = x[2];
-    qv[h][3] = x[3];
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    incl += cb;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > g0);
+    if (hit != 0) {
+      const int f = __builtin_ctzll(hit);
+      b = c + f;
+      cb = __shfl(incl - x, f, 64);
+      break;
+    }
+    cb = __shfl(incl, 63, 64);
   }
 
-  float m[GH], l[GH], acc[GH][DP];
-#pragma unroll
-  for (int h = 0; h < GH; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int j = 0; j < DP; ++j) acc[h][j] = 0.f;
-  }
+  const int64_t row_elems = (int64_t)p.Hkv * D;
+  // per-lane element offsets inside a block of the pool
+  const int64_t koff = (int64_t)n * row_elems + hk * D + 8 * g;  // K: token n, 8 features
+  const int vrow = lane / T::RL;
+  const int vcol = 8 * (lane % T::RL);
+  const int64_t voff = (int64_t)vrow * row_elems + hk * D + vcol;
+  const uint32_t vs_base = (uint32_t)(uintptr_t)vs;
+  const int sl = lane & 15;
+  // transposing-read address: lane (sl, g) supplies row 4g + sl/4, features 4(sl%4) ..+3
+  const uint32_t rd = vs_base + 2u * (uint32_t)((4 * g + (sl >> 2)) * T::PITCH + 4 * (sl & 3));
 
-  for (int i = blk_first; i < blk_last; ++i) {
-    if (i + 1 < blk_last) fetch(i + 1, nk, nv);
-#pragma unroll
-    for (int pass = 0; pass < PASSES; ++pass) {
-      const int t = s_tok + i * kBlock + pass * TPP + tok;
-      const bool valid = t < L && t >= lo;
-      float x[GH];
-#pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[h][w]), as_bf16x2(ck[pass][w]), s, false);
-        // all-reduce over the PARTS lanes of this token row
-        s += dpp_f32<kDppXor1>(s);
-        s += dpp_f32<kDppXor2>(s);
-        s += dpp_f32<kDppHalfMirror>(s);
-        if (PARTS == 16) s += dpp_f32<kDppRor8>(s);
-        x[h] = valid ? s * p.sl2 : kNegInf;
+  int gpos = g0;
+  while (gpos < g1) {
+    const int L = p.lens[b];
+    const int nb = seq_blocks(L, p.max_blocks, p.window);
+    const int end = min(g1, cb + nb);
+    if (gpos >= end) {  // an empty sequence: nothing to read
+      cb += nb;
+      ++b;
+      continue;
+    }
+    const int lo = lo_token(L, p.window);
+    const int first_blk = lo / kBlock + (gpos - cb);   // block index within the sequence
+    const int count = end - gpos;
+    const int* trow = p.table + (int64_t)b * p.max_blocks + first_blk;
+    bool bad = false;
+
+    // K as the A operand of S^T = K Q^T and V rows (RPI rows an instruction);
+    // two register sets, filled alternately.
+    u32x4 kA[T::KC], kB[T::KC], vA[T::VI], vB[T::VI];
+    auto fetch = [&](int i, u32x4 (&rk)[T::KC], u32x4 (&rv)[T::VI]) {
+      int phys = trow[i];
+      if (phys < 0 || phys >= p.num_blocks) {
+        bad = true;
+        phys = 0;
       }
-      bool need = false;
+      const int64_t base = (int64_t)phys * kBlock * row_elems;
+      const uint16_t* kp = p.kc + base + koff;
+      const uint16_t* vp = p.vc + base + voff;
 #pragma unroll
-      for (int h = 0; h < GH; ++h) need = need || (x[h] > m[h] + kLazy);
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      for (int c = 0; c < T::KC; ++c) rk[c] = *reinterpret_cast<const u32x4*>(kp + 32 * c);
 #pragma unroll
-        for (int h = 0; h < GH; ++h) {
-          const float mn = fmaxf(m[h], x[h]);
-          const float a = (mn == kNegInf) ? 1.f : fast_exp2(m[h] - mn);
-          m[h] = mn;
-          l[h] *= a;
+      for (int j = 0; j < T::VI; ++j)
+        rv[j] = *reinterpret_cast<const u32x4*>(vp + (int64_t)j * T::RPI * row_elems);
+    };
+    fetch(0, kA, vA);
+
+    // Q^T as the B operand: lane (n, g) holds head n, the same features as K
+    bf16x8 qf[T::KC];
 #pragma unroll
-          for (int j = 0; j < DP; ++j) acc[h][j] *= a;
+    for (int c = 0; c < T::KC; ++c) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (n < nh)
+        x = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)b * p.Hq + h0 + n) * D + 32 * c + 8 * g);
+      qf[c] = __builtin_bit_cast(bf16x8, x);
+    }
+
+    // O^T tiles (16 features x 16 heads): lane (n, g) holds features 16t + 4g + r
+    // of head n.  m is equal on the four lanes of a head; l is a per-lane partial sum.
+    f32x4 acc[T::NT];
+#pragma unroll
+    for (int t = 0; t < T::NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, mth = kNegInf, lsum = 0.f;
+
+    auto compute = [&](int i, const u32x4 (&rk)[T::KC], const u32x4 (&rv)[T::VI]) {
+      const int t0 = (first_blk + i) * kBlock;             // first token of the block
+      const bool edge = (t0 < lo) || (t0 + kBlock > L);    // wave-uniform
+      // V rows to LDS (tokens outside [lo, L) as zeros: their slots may hold NaN)
+#pragma unroll
+      for (int j = 0; j < T::VI; ++j) {
+        u32x4 v = rv[j];
+        if (edge) {
+          const int tk = t0 + j * T::RPI + vrow;
+          if (tk < lo || tk >= L) v = u32x4{0u, 0u, 0u, 0u};
+        }
+        *reinterpret_cast<u32x4*>(&vs[(j * T::RPI + vrow) * T::PITCH + vcol]) = v;
+      }
+      // S^T: lane (n, g) gets tokens 4g + r of head n
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < T::KC; ++c)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rk[c]), qf[c], s, 0, 0, 0);
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = s[r] * p.sl2;
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tk = t0 + 4 * g + r;
+          if (tk < lo || tk >= L) x[r] = kNegInf;
         }
       }
-      float vf[DP];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t u = valid ? cv[pass][w] : 0u;  // tail slots may hold NaN
-        vf[2 * w] = bf16lo_to_f32(u);
-        vf[2 * w + 1] = bf16hi_to_f32(u);
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      float a = 1.f;
+      if (__builtin_amdgcn_ballot_w64(mx > mth) != 0) {
+        // raise the head's maximum (the same on its four lanes)
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m, mx);
+        a = (mn == kNegInf) ? 1.f : fast_exp2(m - mn);
+        m = mn;
+        mth = mn + kLazy;
       }
+      // unconditional (a == 1 almost always): keeps the accumulators out of the branch
+      lsum *= a;
 #pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        const float pr = (x[h] == kNegInf) ? 0.f : fast_exp2(x[h] - m[h]);
-        l[h] += pr;
+      for (int t = 0; t < T::NT; ++t) acc[t] *= a;
+      float pr[4];
 #pragma unroll
-        for (int j = 0; j < DP; ++j) acc[h][j] += pr * vf[j];
+      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(x[r] - m);
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[r] = (x[r] == kNegInf) ? 0.f : pr[r];
       }
-    }
+      lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      u32x2 pw;
+      pw[0] = pack_bf16x2(pr[0], pr[1]);
+      pw[1] = pack_bf16x2(pr[2], pr[3]);
+      const s16x4 pb = __builtin_bit_cast(s16x4, pw);
+      // O^T += V^T P^T: the transposing LDS read gives lane (n, g) tokens
+      // 4g .. 4g+3 of feature 16t + n
 #pragma unroll
-    for (int pass = 0; pass < PASSES; ++pass) {
-      ck[pass] = nk[pass];
-      cv[pass] = nv[pass];
-    }
-  }
+      for (int t = 0; t < T::NT; ++t) {
+        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(rd + 32u * t));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[t], 0, 0, 0);
+      }
+    };
 
-  // merge the TPP token slots (lanes differing in the bits above PARTS) at a
-  // common max
-#pragma unroll
-  for (int h = 0; h < GH; ++h) {
-    float M = m[h];
-#pragma unroll
-    for (int o = PARTS; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    const float f = (m[h] == kNegInf) ? 0.f : fast_exp2(m[h] - M);
-    float ls = l[h] * f;
-#pragma unroll
-    for (int o = PARTS; o < 64; o <<= 1) ls += __shfl_xor(ls, o, 64);
-#pragma unroll
-    for (int j = 0; j < DP; ++j) {
-      float a = acc[h][j] * f;
-#pragma unroll
-      for (int o = PARTS; o < 64; o <<= 1) a += __shfl_xor(a, o, 64);
-      acc[h][j] = a;
+    // The prefetch index is clamped, so the last block is read twice (the
+    // second time from cache) rather than branching around the loads.
+    for (int i = 0; i < count; i += 2) {
+      fetch(min(i + 1, count - 1), kB, vB);
+      compute(i, kA, vA);
+      if (i + 1 >= count) break;
+      fetch(min(i + 2, count - 1), kA, vA);
+      compute(i + 1, kB, vB);
     }
-    m[h] = M;
-    l[h] = ls;
-  }
-  const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-  if (tok == 0) {
+
+    // l over the four lanes of each head; one partial per (wave, sequence)
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (n < nh) {
+      const int64_t slot = (int64_t)(h0 + n) * p.slots + w + b;
+      float* dst = p.ws_acc + slot * D + 4 * g;
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      const int64_t slot = ((int64_t)b * p.Hq + h0 + h) * p.max_splits + split;
-      float* dst = p.ws_acc + slot * D + part * DP;
-      f32x4 w0, w1;
-      w0[0] = acc[h][0]; w0[1] = acc[h][1]; w0[2] = acc[h][2]; w0[3] = acc[h][3];
-      w1[0] = acc[h][4]; w1[1] = acc[h][5]; w1[2] = acc[h][6]; w1[3] = acc[h][7];
-      reinterpret_cast<f32x4*>(dst)[0] = w0;
-      reinterpret_cast<f32x4*>(dst)[1] = w1;
-      if (part == 0)
+      for (int t = 0; t < T::NT; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t) = acc[t];
+      if (g == 0)
         p.ws_ml[slot] = any_bad ? make_float2(__builtin_nanf(""), __builtin_nanf(""))
-                                : make_float2(m[h], l[h]);
+                                : make_float2(m, lsum);
     }
+    // the waves holding a sequence's first and last blocks record themselves
+    if (hk == 0 && hsub == 0 && lane == 0) {
+      if (gpos == cb) p.ws_seq[b].x = w;
+      if (end == cb + nb) p.ws_seq[b].y = w;
+    }
+    gpos = end;
+    cb += nb;
+    ++b;
   }
 }
 
@@ -243,12 +318,16 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(cons
     if (tid == 0 && p.lse != nullptr) p.lse[(int64_t)b * p.Hq + hq] = __builtin_nanf("");
     return;
   }
-  const int lo = split_lo_token(L, p.window);
-  const int s0 = lo / kSplit;
-  const int s1 = (L + kSplit - 1) / kSplit;
-  const int64_t base = ((int64_t)b * p.Hq + hq) * p.max_splits;
+  // partials of this sequence: slots w + b for the waves w that covered it
+  int s0 = 0, s1 = 0;
+  if (seq_blocks(L, p.max_blocks, p.window) > 0) {
+    const int2 fl = p.ws_seq[b];
+    s0 = max(0, fl.x + b);
+    s1 = min(p.slots, fl.y + b + 1);
+  }
+  const int64_t base = (int64_t)hq * p.slots;
 
-  // common maximum and bad flag over all splits
+  // common maximum and bad flag over all partials
   float M = kNegInf;
   int bad = 0;
   for (int s = s0 + tid; s < s1; s += 64 * kCombineWaves) {
@@ -314,33 +393,35 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(cons
   }
 }
 
-int max_splits_for(int block_size, int max_blocks_per_seq) {
-  const long long tokens = (long long)block_size * max_blocks_per_seq;
-  return (int)((tokens + kSplit - 1) / kSplit);
+int device_cus() {
+  // per-device CU count, looked up once (racing first calls store the same value)
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
 }
 
 }  // namespace
 
 size_t decode_workspace_bytes(int B, int Hq, int d, int block_size, int max_blocks_per_seq) {
-  const size_t slots = (size_t)B * Hq * max_splits_for(block_size, max_blocks_per_seq);
+  (void)block_size;
+  (void)max_blocks_per_seq;
+  const size_t slots = (size_t)Hq * (kMaxWaves + B);
+  const size_t seq = ((size_t)B * sizeof(int2) + 255) / 256 * 256;
   const size_t ml = (slots * sizeof(float2) + 255) / 256 * 256;
-  return ml + slots * (size_t)d * sizeof(float);
-}
-
-template <int D>
-static void launch_split(int gh, const Params& p, dim3 grid, hipStream_t s) {
-  switch (gh) {
-    case 8: hipLaunchKernelGGL((decode_split_kernel<8, D>), grid, dim3(64), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<4, D>), grid, dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<2, D>), grid, dim3(64), 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<1, D>), grid, dim3(64), 0, s, p); break;
-  }
+  return seq + ml + slots * (size_t)d * sizeof(float);
 }
 
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   const int G = a.Hq / a.Hkv;
-  const int gh = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   Params p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.kc = static_cast<const uint16_t*>(a.kcache);
@@ -349,25 +430,33 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
   p.lens = a.seq_lens;
   p.o = static_cast<uint16_t*>(a.out);
   p.lse = a.lse;
+  p.B = a.B;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.group = G;
-  p.hgroups = G / gh;
+  p.hgroups = (G + 15) / 16;
   p.max_blocks = a.max_blocks_per_seq;
   p.num_blocks = a.num_blocks;
   p.window = a.window;
-  p.max_splits = max_splits_for(a.block_size, a.max_blocks_per_seq);
   p.sl2 = a.scale * kLog2e;
-  const size_t slots = (size_t)a.B * a.Hq * p.max_splits;
+  // one wave per resident slot of the whole GPU, shared by the (KV head, head group) pairs
+  const int pairs = a.Hkv * p.hgroups;
+  const int resident = device_cus() * 4 * kWavesPerSimd;
+  p.W = max(1, min(kMaxWaves, resident / pairs));
+  p.slots = kMaxWaves + a.B;
+  char* ws = static_cast<char*>(a.workspace);
+  const size_t seq_bytes = ((size_t)a.B * sizeof(int2) + 255) / 256 * 256;
+  const size_t slots = (size_t)a.Hq * p.slots;
   const size_t ml_bytes = (slots * sizeof(float2) + 255) / 256 * 256;
-  p.ws_ml = static_cast<float2*>(a.workspace);
-  p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ml_bytes);
+  p.ws_seq = reinterpret_cast<int2*>(ws);
+  p.ws_ml = reinterpret_cast<float2*>(ws + seq_bytes);
+  p.ws_acc = reinterpret_cast<float*>(ws + seq_bytes + ml_bytes);
 
-  const dim3 grid1(p.max_splits, a.Hkv * p.hgroups, a.B);
+  const dim3 grid1(p.W, pairs);
   if (a.d == 128)
-    launch_split<128>(gh, p, grid1, stream);
+    hipLaunchKernelGGL(decode_split_kernel<128>, grid1, dim3(64), 0, stream, p);
   else
-    launch_split<64>(gh, p, grid1, stream);
+    hipLaunchKernelGGL(decode_split_kernel<64>, grid1, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid2(a.Hq, a.B);

@@ -50,7 +50,8 @@
  *   - LSE is the natural logarithm of sum_j exp(scale * q.k_j) over the
  *     visible keys, in float32.
  *   - `scale` is used as given (callers normally pass 1/sqrt(d)).
- *   - The library is thread-safe and keeps no state between calls.
+ *   - The library is thread-safe.  Its only state is a per-device cache of the
+ *     compute-unit count, filled on first use.
  */
 #ifndef ATTN_MI355X_ATTN_H
 #define ATTN_MI355X_ATTN_H
@@ -125,7 +126,8 @@ size_t attn_decode_paged_workspace_size(int B, int Hq, int d, int block_size,
  *                attn_decode_paged_workspace_size(...) bytes, owned by the
  *                caller; its contents on entry do not matter
  *
- * block_size must be 16; d in {64, 128}; Hq % Hkv == 0.  A sequence with
+ * block_size must be 16; d in {64, 128}; Hq % Hkv == 0; B <= 65535, Hq <= 65535
+ * and B * max_blocks_per_seq <= INT_MAX (ATTN_E_SHAPE otherwise).  A sequence with
  * seq_len == 0 gets O = 0, LSE = -inf.  A sequence whose length is negative or
  * exceeds max_blocks_per_seq * block_size, or whose table names a block
  * outside [0, num_blocks), gets NaN in out and lse.  Only the used slots of the

@@ -64,10 +64,12 @@ def test_fwd_validation(fn):
 def test_decode_workspace_size():
     L = _lib.lib()
     n = L.attn_decode_paged_workspace_size(16, 32, 128, 16, 2000)
-    # one (m, l) pair and d floats per (sequence, query head, 256-token split)
-    slots = 16 * 32 * 125
-    assert n >= slots * (128 * 4 + 8)
-    assert n < slots * (128 * 4 + 8) + 512
+    # per query head: one (m, l) pair and d floats for each of up to 1024 waves
+    # plus one per sequence (a wave's range may end inside a sequence), and a
+    # (first, last) wave pair per sequence
+    slots = 32 * (1024 + 16)
+    assert n >= slots * (128 * 4 + 8) + 16 * 8
+    assert n < slots * (128 * 4 + 8) + 16 * 8 + 1024
     assert L.attn_decode_paged_workspace_size(16, 32, 128, 32, 2000) == 0   # block size
     assert L.attn_decode_paged_workspace_size(16, 32, 96, 16, 2000) == 0    # head dim
     assert L.attn_decode_paged_workspace_size(16, 32, 64, 16, 0) == 0
@@ -89,6 +91,8 @@ def test_decode_validation():
     assert _dec(ws=None) == _lib.ATTN_E_WORKSPACE
     need = _lib.lib().attn_decode_paged_workspace_size(2, 8, 128, 16, 10)
     assert _dec(ws_bytes=need - 1) == _lib.ATTN_E_WORKSPACE
+    assert _dec(B=65535, maxb=40000) == _lib.ATTN_E_SHAPE  # batch block count beyond int32
+    assert _dec(B=65536) == _lib.ATTN_E_SHAPE
     assert _dec(ptr=None, B=0) == _lib.ATTN_OK
 
 

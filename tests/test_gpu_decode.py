@@ -36,12 +36,18 @@ SMALL = [
     (3, 8, 8, 128, [1000, 999, 5], 100),
     (2, 12, 4, 64, [770, 300], 256),
     (2, 6, 3, 128, [31, 1100], 1),
+    # a query-head group wider than 16 (two waves per KV head: 16 + 8 heads)
+    (2, 24, 1, 128, [700, 65], 0),
+    # more than 64 sequences (several rounds of the on-device prefix sum), with
+    # empty sequences between non-empty ones
+    (70, 4, 2, 64, [0 if i % 7 == 0 else (37 * i) % 300 + 1 for i in range(70)], 0),
 ]
 
 
 def _sid(c):
     B, Hq, Hkv, d, lens, w = c
-    return f"B{B}_h{Hq}x{Hkv}_d{d}_L{'-'.join(map(str, lens))}_w{w}"
+    ls = "-".join(map(str, lens)) if len(lens) <= 4 else f"{len(lens)}seqs"
+    return f"B{B}_h{Hq}x{Hkv}_d{d}_L{ls}_w{w}"
 
 
 @pytest.mark.parametrize("case", SMALL, ids=_sid)
