@@ -25,9 +25,14 @@
 //     vector ALUs; a workgroup barrier swaps the phases (see the schedule
 //     comment at the kernel).
 //   * K/V tiles are staged global -> registers -> LDS (two slots per kind),
-//     group A moving K and group B moving V during their vector phases; LDS
+//     group A moving K and group B moving V during their vector phases, with
+//     two tiles in flight in registers so a load has two phases to land; LDS
 //     rows are padded so that the fragment reads are bank-conflict free, and
 //     fragment reads run several MFMAs ahead of their use.
+//   * The softmax runs stage by stage over the whole tile (32 independent
+//     FMAs, then 32 exponentials, ...) with tree reductions, and the row max
+//     and sum are exchanged with lane l ^ 32 by v_permlane32_swap on the
+//     vector ALU rather than through LDS, which the other wave keeps busy.
 //   * Tiles wholly outside the causal/window band are never visited; only
 //     tiles that cut the band boundary or the key tail pay for the per-element
 //     mask.  The row maximum is raised lazily (only when a row's max grows by
@@ -90,7 +95,8 @@ struct Params {
 // and V(k) in 2k+1; B does M(k) in 2k+1 and V(k) in 2k+2.
 //
 // Staging (two K and two V slots in LDS): A, in V(k), stores K(k+1) and
-// starts loading K(k+2); B, in V(k), stores V(k+1) and starts loading V(k+2).
+// starts loading K(k+3); B, in V(k), stores V(k+1) and starts loading V(k+3)
+// (register sets alternate between even and odd tiles).
 // K(k+1) lands in the slot of K(k-1), last read in slot 2k-1, and is first
 // read in slot 2k+2; V(k+1) lands in the slot of V(k-1), last read in slot
 // 2k+1, and is first read in slot 2k+4.
@@ -148,10 +154,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   const int row0 = gtid / (D / 8);
   constexpr int kRowStep = kGroupThreads / (D / 8);
   const int dst_stride = group_b ? T::VSTRIDE : T::KSTRIDE;
-  u32x4 sreg[T::CHUNKS];
+  u32x4 sreg0[T::CHUNKS], sreg1[T::CHUNKS];  // tiles of even / odd index, two in flight
   auto kslot = [&](int i) { return smem + (i & 1) * T::K_ELEMS; };
   auto vslot = [&](int i) { return smem + 2 * T::K_ELEMS + (i & 1) * T::V_ELEMS; };
-  auto stage_load = [&](int k) {  // tile index k relative to t_begin
+  auto stage_load = [&](int k, u32x4 (&sreg)[T::CHUNKS]) {  // tile index k relative to t_begin
     const int j0 = (t_begin + k) * T::BN;
 #pragma unroll
     for (int c = 0; c < T::CHUNKS; ++c) {
@@ -159,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       sreg[c] = *reinterpret_cast<const u32x4*>(src + (int64_t)j * kv_row + col8 * 8);
     }
   };
-  auto stage_store = [&](int k) {
+  auto stage_store = [&](int k, const u32x4 (&sreg)[T::CHUNKS]) {
     uint16_t* dst = group_b ? vslot(k) : kslot(k);
 #pragma unroll
     for (int c = 0; c < T::CHUNKS; ++c)
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   };
 
   // V(k): softmax of tile k (mask, lazy max, exponentials), then staging
-  auto v_phase = [&](int k) {
+  auto v_phase = [&](int k, u32x4 (&snext)[T::CHUNKS]) {  // snext: registers of tile k+1 (and k+3)
     if (k < n_tiles && !wave_skips(k)) {
       const int j0 = (t_begin + k) * T::BN;
       if (!POS_SCALE) {
@@ -271,28 +277,53 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
                              (p.causal && j0 + T::BN - 1 > qw0 + delta) ||
                              (p.window > 0 && qw0 + kRowsPerWave - 1 + delta - j0 >= p.window);
       if (need_mask) {
+        // visible keys of this lane's row, as offsets from the lane's first key
+        // (key = j0 + 4g + c with c a compile-time constant per register)
         const int pos = qw0 + n + delta;
+        const int base = j0 + 4 * g;
+        int hi = p.Nk - 1 - base;
+        if (p.causal) hi = min(hi, pos - base);
+        if (p.window > 0) {
+          const int lo = pos - p.window + 1 - base;
 #pragma unroll
-        for (int kb = 0; kb < T::NKB; ++kb)
+          for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-            bool vis = key < p.Nk;
-            if (p.causal) vis = vis && key <= pos;
-            if (p.window > 0) vis = vis && (pos - key) < p.window;
-            if (!vis) st[kb][r] = kNegInf;
-          }
+            for (int r = 0; r < 16; ++r) {
+              const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+              if (c > hi || c < lo) st[kb][r] = kNegInf;
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+              if (c > hi) st[kb][r] = kNegInf;
+            }
+        }
       }
       // online softmax with a lazily raised maximum: the stored max only moves
       // when some row's max exceeds it by more than 2^8, so most tiles skip
       // the accumulator rescale; probabilities stay <= 2^8, and the final
       // division uses the sum taken at the same max, so the result is exact.
-      float mx = kNegInf;
+      // row max as a tree (independent chains keep the VALU pipeline full)
+      float mq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mq[j] = fmaxf(st[0][4 * j], st[0][4 * j + 1]);
 #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-      mx = fmaxf(mx, swap_halves(mx));
+        for (int r = 0; r < 16; ++r) {
+          if (kb == 0 && (r & 3) < 2) continue;
+          mq[r >> 2] = fmaxf(mq[r >> 2], st[kb][r]);
+        }
+      float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+      {  // max with lane l ^ 32 (the same row) on the VALU
+        float a = mx, b = mx;
+        // inline asm: the compiler folds a max of the builtin's two results away
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+        mx = fmaxf(a, b);
+      }
       if (POS_SCALE) mx *= p.sl2;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
         const float m_new = fmaxf(m_run, mx);
@@ -305,54 +336,73 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
         m_run = m_new;
       }
       const float m_use = (m_run == kNegInf) ? 0.f : m_run;  // row with nothing visible yet
-      float rs = 0.f;
+      // exponentials in place, stage by stage, so that each stage is 32
+      // independent instructions
 #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float p0, p1;
-          if (POS_SCALE) {
-            p0 = fast_exp2(fmaf(st[kb][2 * i], p.sl2, -m_use));
-            p1 = fast_exp2(fmaf(st[kb][2 * i + 1], p.sl2, -m_use));
-          } else {
-            p0 = fast_exp2(st[kb][2 * i] - m_use);
-            p1 = fast_exp2(st[kb][2 * i + 1] - m_use);
-          }
-          pk[kb][i] = pack_bf16x2(p0, p1);
-          rs += p0 + p1;  // float32 sum: the LSE must reproduce exp(S - LSE) to fp32
-        }
-      l_run += rs;
+        for (int r = 0; r < 16; ++r)
+          st[kb][r] = POS_SCALE ? fmaf(st[kb][r], p.sl2, -m_use) : st[kb][r] - m_use;
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[kb][r] = fast_exp2(st[kb][r]);
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pk[kb][i] = pack_bf16x2(st[kb][2 * i], st[kb][2 * i + 1]);
+      // float32 row sum (the LSE must reproduce exp(S - LSE) to fp32), as a tree
+      float rq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rq[r & 3] += st[kb][r];
+      l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
     }
-    if (k + 1 < n_tiles) stage_store(k + 1);
-    if (k + 2 < n_tiles) stage_load(k + 2);
+    if (k + 1 < n_tiles) stage_store(k + 1, snext);
+    if (k + 3 < n_tiles) stage_load(k + 3, snext);
   };
 
   // prologue: K(0) in LDS; A holds K(1), B holds V(0) in registers
   if (n_tiles > 0) {
     if (!group_b) {
-      stage_load(0);
-      stage_store(0);
-      if (n_tiles > 1) stage_load(1);
+      stage_load(0, sreg0);
+      stage_store(0, sreg0);
+      if (n_tiles > 1) stage_load(1, sreg1);
+      if (n_tiles > 2) stage_load(2, sreg0);
     } else {
-      stage_load(0);
+      stage_load(0, sreg0);
     }
   }
   __syncthreads();
   if (group_b) {  // B's V(-1): store V(0), start V(1)
-    if (n_tiles > 0) stage_store(0);
-    if (n_tiles > 1) stage_load(1);
+    if (n_tiles > 0) stage_store(0, sreg0);
+    if (n_tiles > 1) stage_load(1, sreg1);
+    if (n_tiles > 2) stage_load(2, sreg0);
     __syncthreads();
   }
-  for (int k = 0; k <= n_tiles; ++k) {
+  // Make the Q loads complete here, once: otherwise the wait for them is placed
+  // inside the loop, where it also waits for the staging loads in flight.
+#pragma unroll
+  for (int c = 0; c < T::KC; ++c) asm volatile("" ::"v"(qf[c]));
+  // two tiles per trip so that the staging registers alternate statically
+  for (int k = 0; k <= n_tiles; k += 2) {
     m_phase(k);
     __syncthreads();
-    v_phase(k);
+    v_phase(k, sreg1);
+    __syncthreads();
+    if (k + 1 > n_tiles) break;
+    m_phase(k + 1);
+    __syncthreads();
+    v_phase(k + 1, sreg0);
     __syncthreads();
   }
   if (!group_b) __syncthreads();  // A's extra barrier matches B's first one
 
   // epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
-  const float l_tot = l_run + swap_halves(l_run);
+  float la = l_run, lb = l_run;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(la), "+v"(lb));
+  const float l_tot = la + lb;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int row = qw0 + n;
   if (row < p.Nq) {
