@@ -27,6 +27,8 @@ int check_fwd(const void* q, const void* k, const void* v, const void* out, int 
   if (window > 0 && !causal) return ATTN_E_MASK;
   if (causal && Nq > Nk) return ATTN_E_SHAPE;
   if (grid > INT_MAX) return ATTN_E_SHAPE;
+  // a 64-key tile of one head is addressed with 32-bit byte offsets
+  if ((long long)Hkv * d > (1LL << 22)) return ATTN_E_SHAPE;
   return ATTN_OK;
 }
 

@@ -24,11 +24,14 @@
 //     one issues the matrix products, the other computes its softmax on the
 //     vector ALUs; a workgroup barrier swaps the phases (see the schedule
 //     comment at the kernel).
-//   * K/V tiles are staged global -> registers -> LDS (two slots per kind),
-//     group A moving K and group B moving V during their vector phases, with
-//     two tiles in flight in registers so a load has two phases to land; LDS
-//     rows are padded so that the fragment reads are bank-conflict free, and
-//     fragment reads run several MFMAs ahead of their use.
+//   * K/V tiles go from HBM/L2 straight into LDS with buffer loads that
+//     write LDS (no registers, no LDS store instructions), into a ring of
+//     kSlots tile slots per kind, so that a load has 2*(kSlots-1) phases to
+//     land.  Each load instruction fills 1 KiB of LDS contiguously; the 16-byte
+//     pieces of a row are XOR-swizzled (each lane fetches the piece that
+//     belongs at its LDS position) so that the fragment reads of K and the
+//     transposed reads of V are bank-conflict free.  Rows past the last key
+//     read as zero (buffer range check).
 //   * The softmax runs stage by stage over the whole tile (32 independent
 //     FMAs, then 32 exponentials, ...) with tree reductions, and the row max
 //     and sum are exchanged with lane l ^ 32 by v_permlane32_swap on the
@@ -40,6 +43,8 @@
 //   * Work groups are ordered heavy-first (last query tiles first) inside a
 //     head and remapped so that the tiles of one head share an XCD (and its
 //     L2), since they all stream the same K/V.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -50,11 +55,12 @@ constexpr int kWaves = 8;                    // two groups of 4, one wave of eac
 constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;   // query rows per work group
 constexpr int kThreads = kWaves * 64;
-constexpr int kGroupThreads = kThreads / 2;
+constexpr int kSlots = 4;                    // LDS tile slots per kind (K, V)
 constexpr float kLazy = 8.0f;  // rescale only when a row max grows by more than 2^8
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct Tile {
@@ -63,17 +69,20 @@ struct Tile {
   static constexpr int NDB = D / 32;                 // 32-feature blocks of O^T
   static constexpr int KC = D / 16;                  // k-chunks of K Q^T
   static constexpr int VC = BN / 16;                 // k-chunks of V^T P^T
-  // Row strides in LDS (bf16 elements).  K rows are read 16 bytes per lane
-  // down 16 consecutive rows: a stride of 16*odd bytes spreads them over all
-  // banks.  V rows are read with the transposing LDS load, 4 rows x 64 bytes
-  // per half wave: a stride of 64 or 192 bytes past a multiple of 256 does.
-  static constexpr int KSTRIDE = D + 8;
-  static constexpr int VSTRIDE = D + 32;
-  static constexpr int K_ELEMS = BN * KSTRIDE;
-  static constexpr int V_ELEMS = BN * VSTRIDE;
-  static constexpr int CHUNKS = BN * D / 8 / kGroupThreads;  // 16-byte pieces per group thread
-  static_assert(CHUNKS * kGroupThreads * 8 == BN * D, "staging must cover the tile");
-  static_assert((VSTRIDE * 2) % 128 == 64, "V rows must fall 64 bytes apart modulo 128");
+  static constexpr int ROWB = D * 2;                 // bytes of one key row in LDS
+  static constexpr int TILEB = BN * ROWB;            // bytes of one K or V tile
+  static constexpr int NLD = TILEB / 1024;           // 1 KiB load instructions per tile
+  static constexpr int LPW = NLD / kWaves;           // per wave, per kind
+  static constexpr int LDS_BYTES = 2 * kSlots * TILEB;
+  static_assert(LPW * kWaves == NLD, "every wave moves the same share of a tile");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  // 16-byte piece swizzles (XOR on the piece index within a row).
+  // K is read 16 bytes per lane down 16 consecutive rows at one logical
+  // piece: the XOR spreads those rows over all 64 banks.  V is read with the
+  // transposing load, 8 bytes per lane, 4 consecutive rows x 64 bytes per 32
+  // lanes: the XOR moves each of the 4 rows to a different 64-byte quarter.
+  __device__ static int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  __device__ static int vswz(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 };
 
 struct Params {
@@ -86,6 +95,53 @@ struct Params {
   float sl2;  // scale * log2(e): scores are kept in the base-2 domain
 };
 
+// Buffer resource for raw (unswizzled) 32-bit addressing: loads at byte
+// offsets >= bytes return zero and touch no memory.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(a));
+  r[1] = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu);
+  r[2] = static_cast<int>(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from the buffer into LDS at lds_base + OFF + 16 * lane.
+// The compiler does not see this load: the kernel waits for it itself
+// (wait_vm) before the barrier that hands the tile to the other waves.  M0
+// (the LDS address of the load) is set inside the asm; nothing else in these
+// kernels uses M0.
+template <uint32_t OFF>
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, int voffset, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(rsrc), "s"(lds_base), "n"(OFF) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (N < 16) with the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Work-group barrier that orders LDS only (global memory needs no fence
+// here: the LDS-writing loads are waited for explicitly).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ bool unrolled_while(F&& f) {
+  if constexpr (I < N) {
+    if (!f(std::integral_constant<int, I>{})) return false;
+    return unrolled_while<I + 1, N>(f);
+  }
+  return true;
+}
+
 // Schedule ("ping-pong").  The 8 waves form two groups, A = waves 0-3 and
 // B = waves 4-7, so each SIMD runs one wave of each.  Every wave alternates
 // an MFMA phase, M(k) = scores of tile k and P V of tile k-1, with a vector
@@ -94,25 +150,30 @@ struct Params {
 // the phases swap at every barrier.  Barrier slots: A does M(k) in slot 2k
 // and V(k) in 2k+1; B does M(k) in 2k+1 and V(k) in 2k+2.
 //
-// Staging (two K and two V slots in LDS): A, in V(k), stores K(k+1) and
-// starts loading K(k+3); B, in V(k), stores V(k+1) and starts loading V(k+3)
-// (register sets alternate between even and odd tiles).
-// K(k+1) lands in the slot of K(k-1), last read in slot 2k-1, and is first
-// read in slot 2k+2; V(k+1) lands in the slot of V(k-1), last read in slot
-// 2k+1, and is first read in slot 2k+4.
+// Loads: in every even slot 2m each wave issues its share of "batch m" =
+// K(m-1+S) and V(m-2+S) (S = kSlots), into the slots of K(m-1) and V(m-2),
+// which were last read in slot 2m-1.  Group A issues at the start of its
+// M(m), group B at the start of its V(m-1).  Batch m is first read in slot
+// 2m+2S-2, so every wave waits for its own loads of batch m at the end of
+// slot 2m+2S-3 (the S-2 later batches may stay in flight), before the
+// barrier.  Loads of tiles past the last one read nothing and fill free slots.
 //
 // POS_SCALE: scale > 0, so the row maximum of scale*s is scale * max(s) and the
 // scaling folds into the exponent's FMA.  Otherwise every score is scaled first.
 template <int D, bool POS_SCALE>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (T::K_ELEMS + T::V_ELEMS)];
+  constexpr int S = kSlots;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
+  // K slots at [0, S*TILEB), V slots at [S*TILEB, 2*S*TILEB)
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  lds_u8* const lds = (lds_u8*)smem;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool group_b = wave >= kWaves / 2;
-  const int gtid = tid & (kGroupThreads - 1);
   const int n = lane & 31;  // query row within the wave / MFMA column
   const int g = lane >> 5;  // k-half of the MFMA operands
 
@@ -143,44 +204,71 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     for (int c = 0; c < T::KC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + c * 16);
   }
 
-  // Staging: group A moves K tiles, group B V tiles.  Piece c of a group
-  // thread is row (gtid + c*256) / (D/8) of the tile, 16-byte column
-  // gtid % (D/8).  Rows past the last key re-read the last key: their scores
-  // are masked and their probabilities are exactly zero, so a finite duplicate
-  // contributes nothing.
-  const int64_t kv_row = (int64_t)p.Hkv * D;
-  const uint16_t* src = (group_b ? p.v : p.k) + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
-  const int col8 = gtid % (D / 8);
-  const int row0 = gtid / (D / 8);
-  constexpr int kRowStep = kGroupThreads / (D / 8);
-  const int dst_stride = group_b ? T::VSTRIDE : T::KSTRIDE;
-  u32x4 sreg0[T::CHUNKS], sreg1[T::CHUNKS];  // tiles of even / odd index, two in flight
-  auto kslot = [&](int i) { return smem + (i & 1) * T::K_ELEMS; };
-  auto vslot = [&](int i) { return smem + 2 * T::K_ELEMS + (i & 1) * T::V_ELEMS; };
-  auto stage_load = [&](int k, u32x4 (&sreg)[T::CHUNKS]) {  // tile index k relative to t_begin
-    const int j0 = (t_begin + k) * T::BN;
+  // ---- loads into LDS.  Instruction i of a tile fills LDS bytes
+  // [1024 i, 1024 i + 1024) of the slot; lane L's 16 bytes land at 1024 i + 16 L,
+  // which is row r = (1024 i + 16 L) / ROWB, physical piece c; the lane
+  // fetches logical piece c ^ swizzle(r) of key row r.
+  const int64_t kv_row = (int64_t)p.Hkv * D;                 // elements between keys
+  const uint32_t kv_row_b = static_cast<uint32_t>(kv_row * 2);
+  const int64_t head_off = (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
+  const uint16_t* kbase = p.k + head_off;
+  const uint16_t* vbase = p.v + head_off;
+  int koff[T::LPW], voff[T::LPW];
 #pragma unroll
-    for (int c = 0; c < T::CHUNKS; ++c) {
-      const int j = min(j0 + row0 + c * kRowStep, p.Nk - 1);
-      sreg[c] = *reinterpret_cast<const u32x4*>(src + (int64_t)j * kv_row + col8 * 8);
+  for (int j = 0; j < T::LPW; ++j) {
+    const int pos = (wave * T::LPW + j) * 1024 + lane * 16;
+    const int r = pos / T::ROWB;
+    const int c = (pos % T::ROWB) >> 4;
+    koff[j] = r * (int)kv_row_b + ((c ^ T::kswz(r)) << 4);
+    voff[j] = r * (int)kv_row_b + ((c ^ T::vswz(r)) << 4);
+  }
+  // this wave's share of tile t (relative to t_begin) of one kind into the
+  // LDS slot at byte DST (K slots first, then V slots)
+  const uint32_t lds_wave = lds0 + wave * T::LPW * 1024;
+  const uint32_t tile_b = (uint32_t)T::BN * kv_row_b;  // bytes of a whole tile's rows
+  auto issue = [&](auto DST, const uint16_t* base, const int (&off)[T::LPW], int t) {
+    constexpr uint32_t dst = decltype(DST)::value;
+    const int j0 = (t_begin + t) * T::BN;
+    uint32_t bytes = 0;  // loads at or past this offset read zero
+    if (t < n_tiles) {
+      // the last valid byte is the end of the head's part of key row Nk-1
+      const int rows = p.Nk - j0;  // >= 1
+      bytes = rows >= T::BN ? tile_b : (uint32_t)(rows - 1) * kv_row_b + T::ROWB;
     }
+    const i32x4 rsrc = make_rsrc(base + (int64_t)j0 * kv_row, bytes);
+    load_lds16<dst>(rsrc, off[0], lds_wave);
+    if constexpr (T::LPW > 1) load_lds16<dst + 1024>(rsrc, off[1], lds_wave);
+    static_assert(T::LPW <= 2, "load count per wave");
   };
-  auto stage_store = [&](int k, const u32x4 (&sreg)[T::CHUNKS]) {
-    uint16_t* dst = group_b ? vslot(k) : kslot(k);
-#pragma unroll
-    for (int c = 0; c < T::CHUNKS; ++c)
-      *reinterpret_cast<u32x4*>(dst + (row0 + c * kRowStep) * dst_stride + col8 * 8) = sreg[c];
+  auto issue_k = [&](auto SLOT, int t) {
+    issue(std::integral_constant<uint32_t, decltype(SLOT)::value * T::TILEB>{}, kbase, koff, t);
   };
+  auto issue_v = [&](auto SLOT, int t) {
+    issue(std::integral_constant<uint32_t, (S + decltype(SLOT)::value) * T::TILEB>{}, vbase, voff, t);
+  };
+  using std::integral_constant;
 
-  // Transposed V reads: for MFMA k-chunk kc and feature block db, lane
+  // ---- LDS fragment offsets (bytes from the LDS base, per lane; slots and
+  // blocks are added as immediates)
+  // K: row n of the 32-key block, logical piece 2 kc + g
+  uint32_t kaddr[T::KC];
+#pragma unroll
+  for (int kc = 0; kc < T::KC; ++kc) kaddr[kc] = n * T::ROWB + (((2 * kc + g) ^ T::kswz(n)) << 4);
+  // V (transposing read): for MFMA k-chunk kc and feature block db, lane
   // (group G = lane/16, s = lane%16) points at key kc*16 + (G/2)*4 + s/4
   // (+8 for the second read) and features db*32 + 16*(G%2) + 4*(s%4).  The
   // hardware hands lane 4r+c of each 16-lane group the 4 keys of source lanes
   // r, r+4, r+8, r+12 at feature 4r+c, which is V^T in the operand layout, with
   // lane group g holding keys {g*4..g*4+3, 8+g*4..8+g*4+3} of the chunk.
+  // The swizzle of a key row depends only on the key modulo 4.
   const int G16 = lane >> 4, s16 = lane & 15;
   const int vt_key = (G16 >> 1) * 4 + (s16 >> 2);
-  const int vt_col = 16 * (G16 & 1) + 4 * (s16 & 3);
+  uint32_t vaddr[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) {
+    const int piece = db * 4 + 2 * (G16 & 1) + ((s16 & 3) >> 1);
+    vaddr[db] = S * T::TILEB + vt_key * T::ROWB + ((piece ^ T::vswz(vt_key)) << 4) + 8 * (s16 & 1);
+  }
 
   auto wave_skips = [&](int k) {
     const int j0 = (t_begin + k) * T::BN;
@@ -200,23 +288,29 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
 
   // M(k): scores of tile k, then P V of tile k-1.  The fragment reads run a
   // few MFMAs ahead of their use so that the LDS latency stays hidden.
-  auto m_phase = [&](int k) {
+  // U = k mod S (compile time), so every LDS slot offset is an immediate.
+  auto m_phase = [&](auto U, int k) {
+    constexpr int u = decltype(U)::value;
+    if (!group_b) {  // batch k
+      issue_k(integral_constant<int, (u + S - 1) % S>{}, k - 1 + S);
+      issue_v(integral_constant<int, (u + S - 2) % S>{}, k - 2 + S);
+    }
     __builtin_amdgcn_s_setprio(1);
     if (k < n_tiles && !wave_skips(k)) {
-      const uint16_t* ks = kslot(k) + n * T::KSTRIDE + g * 8;
       constexpr int NQK = T::NKB * T::KC;  // MFMAs of the score tile
       constexpr int LA = 8;                // reads in flight ahead
       bf16x8 kf[NQK];
+      auto kld = [&](int i) {
+        const uint32_t a = kaddr[i % T::KC] + u * T::TILEB + (i / T::KC) * 32 * T::ROWB;
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
+      };
 #pragma unroll
-      for (int i = 0; i < LA; ++i)
-        kf[i] = *reinterpret_cast<const bf16x8*>(ks + (i / T::KC) * 32 * T::KSTRIDE + (i % T::KC) * 16);
+      for (int i = 0; i < LA; ++i) kf[i] = kld(i);
 #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb) st[kb] = f32x16{};
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
-        if (i + LA < NQK)
-          kf[i + LA] = *reinterpret_cast<const bf16x8*>(
-              ks + ((i + LA) / T::KC) * 32 * T::KSTRIDE + ((i + LA) % T::KC) * 16);
+        if (i + LA < NQK) kf[i + LA] = kld(i + LA);
         st[i / T::KC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i % T::KC], st[i / T::KC], 0, 0, 0);
       }
       // keep LA reads in flight: reads, then alternate one MFMA / one read
@@ -228,14 +322,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       }
     }
     if (k >= 1 && !wave_skips(k - 1)) {
-      const uint16_t* vrow = vslot(k - 1) + vt_key * T::VSTRIDE + vt_col;
+      constexpr int vs = (u + S - 1) % S;  // slot of V(k-1)
       constexpr int NPV = T::VC * T::NDB;  // MFMAs of the P V update
       constexpr int LA = 6;
       bf16x8 vf[NPV];
       auto vread = [&](int i) {  // i = kc * NDB + db
-        const uint16_t* r = vrow + (i / T::NDB) * 16 * T::VSTRIDE + (i % T::NDB) * 32;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)r);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r + 8 * T::VSTRIDE));
+        const uint32_t a = vaddr[i % T::NDB] + vs * T::TILEB + (i / T::NDB) * 16 * T::ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a + 8 * T::ROWB));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
 #pragma unroll
@@ -261,10 +355,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       }
     }
     __builtin_amdgcn_s_setprio(0);
+    if (group_b) wait_vm<2 * T::LPW * (S - 2)>();
   };
 
-  // V(k): softmax of tile k (mask, lazy max, exponentials), then staging
-  auto v_phase = [&](int k, u32x4 (&snext)[T::CHUNKS]) {  // snext: registers of tile k+1 (and k+3)
+  // V(k): softmax of tile k (mask, lazy max, exponentials)
+  auto v_phase = [&](auto U, int k) {
+    constexpr int u = decltype(U)::value;
+    if (group_b) {  // batch k + 1
+      issue_k(integral_constant<int, u>{}, k + S);
+      issue_v(integral_constant<int, (u + S - 1) % S>{}, k - 1 + S);
+    }
     if (k < n_tiles && !wave_skips(k)) {
       const int j0 = (t_begin + k) * T::BN;
       if (!POS_SCALE) {
@@ -319,10 +419,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
         }
       float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
       {  // max with lane l ^ 32 (the same row) on the VALU
-        float a = mx, b = mx;
+        float a = mx, bb = mx;
         // inline asm: the compiler folds a max of the builtin's two results away
-        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-        mx = fmaxf(a, b);
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(bb));
+        mx = fmaxf(a, bb);
       }
       if (POS_SCALE) mx *= p.sl2;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
@@ -359,45 +459,36 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
         for (int r = 0; r < 16; ++r) rq[r & 3] += st[kb][r];
       l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
     }
-    if (k + 1 < n_tiles) stage_store(k + 1, snext);
-    if (k + 3 < n_tiles) stage_load(k + 3, snext);
+    if (!group_b) wait_vm<2 * T::LPW * (S - 2)>();
   };
 
-  // prologue: K(0) in LDS; A holds K(1), B holds V(0) in registers
-  if (n_tiles > 0) {
-    if (!group_b) {
-      stage_load(0, sreg0);
-      stage_store(0, sreg0);
-      if (n_tiles > 1) stage_load(1, sreg1);
-      if (n_tiles > 2) stage_load(2, sreg0);
-    } else {
-      stage_load(0, sreg0);
-    }
-  }
-  __syncthreads();
-  if (group_b) {  // B's V(-1): store V(0), start V(1)
-    if (n_tiles > 0) stage_store(0, sreg0);
-    if (n_tiles > 1) stage_load(1, sreg1);
-    if (n_tiles > 2) stage_load(2, sreg0);
-    __syncthreads();
-  }
-  // Make the Q loads complete here, once: otherwise the wait for them is placed
-  // inside the loop, where it also waits for the staging loads in flight.
+  // prologue: K(0..S-2) and V(0..S-3) in LDS before the first barrier
+  unrolled_while<0, S - 1>([&](auto T_) { issue_k(T_, decltype(T_)::value); return true; });
+  unrolled_while<0, S - 2>([&](auto T_) { issue_v(T_, decltype(T_)::value); return true; });
+  wait_vm<0>();  // also completes the Q loads, once, outside the loop
 #pragma unroll
   for (int c = 0; c < T::KC; ++c) asm volatile("" ::"v"(qf[c]));
-  // two tiles per trip so that the staging registers alternate statically
-  for (int k = 0; k <= n_tiles; k += 2) {
-    m_phase(k);
-    __syncthreads();
-    v_phase(k, sreg1);
-    __syncthreads();
-    if (k + 1 > n_tiles) break;
-    m_phase(k + 1);
-    __syncthreads();
-    v_phase(k + 1, sreg0);
-    __syncthreads();
+  lds_barrier();
+  if (group_b) {  // B's slot 0 (its "V(-1)"): batch 0
+    issue_k(integral_constant<int, S - 1>{}, S - 1);
+    issue_v(integral_constant<int, S - 2>{}, S - 2);
+    lds_barrier();
   }
-  if (!group_b) __syncthreads();  // A's extra barrier matches B's first one
+  // S tiles per trip so that every LDS slot index is a compile-time constant;
+  // the last step (k = n_tiles) only finishes P V of the last tile
+  for (int k0 = 0;; k0 += S) {
+    const bool more = unrolled_while<0, S>([&](auto U) {
+      const int k = k0 + decltype(U)::value;
+      m_phase(U, k);
+      lds_barrier();
+      v_phase(U, k);
+      lds_barrier();
+      return k < n_tiles;
+    });
+    if (!more) break;
+  }
+  if (!group_b) lds_barrier();  // A's extra barrier matches B's first one
+  wait_vm<0>();  // loads past the last tile still land in LDS: drain them
 
   // epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
   float la = l_run, lb = l_run;

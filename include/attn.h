@@ -83,7 +83,8 @@ enum {
  *   lse  [B, Hq, Nq]      float32, or NULL to skip it
  *
  * Sizes: B, Nq, Nk >= 0 (B == 0 or Nq == 0 is a no-op; Nk == 0 gives O = 0,
- * LSE = -inf); Hq, Hkv >= 1 with Hq % Hkv == 0; d in {64, 128}.  Pointers of
+ * LSE = -inf); Hq, Hkv >= 1 with Hq % Hkv == 0; d in {64, 128}; Hkv * d <=
+ * 4194304 (key tiles are addressed with 32-bit byte offsets).  Pointers of
  * tensors with no elements may be NULL; the others must not be (ATTN_E_NULL).
  * causal: 0 or 1; causal requires Nq <= Nk.  window: <= 0 for none, else the
  * number of keys kept (requires causal).
