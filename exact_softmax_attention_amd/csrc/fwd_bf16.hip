@@ -38,8 +38,9 @@
 //     vector ALU rather than through LDS, which the other wave keeps busy.
 //   * Tiles wholly outside the causal/window band are never visited; only
 //     tiles that cut the band boundary or the key tail pay for the per-element
-//     mask.  The row maximum is raised lazily (only when a row's max grows by
-//     more than 2^8), so most tiles skip the accumulator rescale.
+//     mask.  The exponentials are taken against the stored row maximum, which
+//     is raised only when a tile's terms would grow past 2^8, so most tiles
+//     skip both the row maximum and the accumulator rescale.
 //   * Work groups are ordered heavy-first (last query tiles first) inside a
 //     head and remapped so that the tiles of one head share an XCD (and its
 //     L2), since they all stream the same K/V.
@@ -56,7 +57,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;   // query rows per work group
 constexpr int kThreads = kWaves * 64;
 constexpr int kSlots = 4;                    // LDS tile slots per kind (K, V)
-constexpr float kLazy = 8.0f;  // rescale only when a row max grows by more than 2^8
+constexpr float kRaise = 256.0f;  // raise the stored max when a partial row sum exceeds this
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -111,11 +112,13 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // The compiler does not see this load: the kernel waits for it itself
 // (wait_vm) before the barrier that hands the tile to the other waves.  M0
 // (the LDS address of the load) is set inside the asm; nothing else in these
-// kernels uses M0.
+// kernels uses M0.  The scalar add also writes SCC, so SCC is declared
+// clobbered: the compiler may otherwise keep a compare result in SCC across
+// the asm.
 template <uint32_t OFF>
 __device__ __forceinline__ void load_lds16(i32x4 rsrc, int voffset, uint32_t lds_base) {
   asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voffset), "s"(rsrc), "s"(lds_base), "n"(OFF) : "memory", "m0");
+               :: "v"(voffset), "s"(rsrc), "s"(lds_base), "n"(OFF) : "memory", "m0", "scc");
 }
 
 // s_waitcnt vmcnt(N) (N < 16) with the other counters left alone.
@@ -150,13 +153,22 @@ __device__ __forceinline__ bool unrolled_while(F&& f) {
 // the phases swap at every barrier.  Barrier slots: A does M(k) in slot 2k
 // and V(k) in 2k+1; B does M(k) in 2k+1 and V(k) in 2k+2.
 //
-// Loads: in every even slot 2m each wave issues its share of "batch m" =
-// K(m-1+S) and V(m-2+S) (S = kSlots), into the slots of K(m-1) and V(m-2),
-// which were last read in slot 2m-1.  Group A issues at the start of its
-// M(m), group B at the start of its V(m-1).  Batch m is first read in slot
-// 2m+2S-2, so every wave waits for its own loads of batch m at the end of
-// slot 2m+2S-3 (the S-2 later batches may stay in flight), before the
-// barrier.  Loads of tiles past the last one read nothing and fill free slots.
+// Loads: "batch m" = K(m-1+S) and V(m-2+S) (S = kSlots), into the slots of
+// K(m-1) and V(m-2), which were last read in slot 2m-1.  Each wave issues its
+// share of batch m at the start of its own M(m): group A in slot 2m, group B
+// in slot 2m+1 (the MFMA phase leaves the wave's issue slots idle).  Batch m
+// is first read in slot 2m+2S-2, so every wave waits for its own loads of
+// batch m at the end of slot 2m+2S-3 (the S-2 later batches may stay in
+// flight), before the barrier.  Loads of tiles past the last one read nothing
+// and fill free slots.
+//
+// Softmax: the exponentials are first taken against the stored row maximum.
+// The online softmax is exact for any reference value that keeps the terms
+// finite, so the stored maximum only has to be raised when a term would grow
+// large: when a lane's partial row sum of the tile exceeds 2^8 (or is not
+// finite, as on a row's first visible tile), the tile is redone with the true
+// row maximum, and the accumulator and sum are rescaled.  Most tiles skip
+// the row maximum altogether.
 //
 // POS_SCALE: scale > 0, so the row maximum of scale*s is scale * max(s) and the
 // scaling folds into the exponent's FMA.  Otherwise every score is scaled first.
@@ -222,29 +234,35 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     koff[j] = r * (int)kv_row_b + ((c ^ T::kswz(r)) << 4);
     voff[j] = r * (int)kv_row_b + ((c ^ T::vswz(r)) << 4);
   }
-  // this wave's share of tile t (relative to t_begin) of one kind into the
-  // LDS slot at byte DST (K slots first, then V slots)
+  // Each wave issues the tiles of one kind in order (K(0), K(1), ... and
+  // V(0), V(1), ...), so a running byte address per kind is enough; the range
+  // of a tile is whole except for the last visible one, and zero past it.
   const uint32_t lds_wave = lds0 + wave * T::LPW * 1024;
   const uint32_t tile_b = (uint32_t)T::BN * kv_row_b;  // bytes of a whole tile's rows
-  auto issue = [&](auto DST, const uint16_t* base, const int (&off)[T::LPW], int t) {
+  uint32_t last_b = 0;  // bytes of the last visible tile: up to the end of key row Nk-1
+  if (n_tiles > 0) {
+    const int rows = p.Nk - (t_begin + n_tiles - 1) * T::BN;  // >= 1
+    last_b = rows >= T::BN ? tile_b : (uint32_t)(rows - 1) * kv_row_b + T::ROWB;
+  }
+  const uint8_t* knext = reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t_begin * tile_b;
+  const uint8_t* vnext = reinterpret_cast<const uint8_t*>(vbase) + (int64_t)t_begin * tile_b;
+  int kt = 0, vt = 0;  // index of the next tile of each kind
+  auto issue = [&](auto DST, const uint8_t*& next, int& t, const int (&off)[T::LPW]) {
     constexpr uint32_t dst = decltype(DST)::value;
-    const int j0 = (t_begin + t) * T::BN;
-    uint32_t bytes = 0;  // loads at or past this offset read zero
-    if (t < n_tiles) {
-      // the last valid byte is the end of the head's part of key row Nk-1
-      const int rows = p.Nk - j0;  // >= 1
-      bytes = rows >= T::BN ? tile_b : (uint32_t)(rows - 1) * kv_row_b + T::ROWB;
-    }
-    const i32x4 rsrc = make_rsrc(base + (int64_t)j0 * kv_row, bytes);
+    const uint32_t bytes = t < n_tiles - 1 ? tile_b : (t == n_tiles - 1 ? last_b : 0u);
+    const i32x4 rsrc = make_rsrc(next, bytes);
     load_lds16<dst>(rsrc, off[0], lds_wave);
     if constexpr (T::LPW > 1) load_lds16<dst + 1024>(rsrc, off[1], lds_wave);
     static_assert(T::LPW <= 2, "load count per wave");
+    next += tile_b;
+    ++t;
   };
-  auto issue_k = [&](auto SLOT, int t) {
-    issue(std::integral_constant<uint32_t, decltype(SLOT)::value * T::TILEB>{}, kbase, koff, t);
+  // the next K tile into K slot SLOT, the next V tile into V slot SLOT
+  auto issue_k = [&](auto SLOT) {
+    issue(std::integral_constant<uint32_t, decltype(SLOT)::value * T::TILEB>{}, knext, kt, koff);
   };
-  auto issue_v = [&](auto SLOT, int t) {
-    issue(std::integral_constant<uint32_t, (S + decltype(SLOT)::value) * T::TILEB>{}, vbase, voff, t);
+  auto issue_v = [&](auto SLOT) {
+    issue(std::integral_constant<uint32_t, (S + decltype(SLOT)::value) * T::TILEB>{}, vnext, vt, voff);
   };
   using std::integral_constant;
 
@@ -284,87 +302,94 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) acc[db] = f32x16{};
   f32x16 st[T::NKB];          // scores of the tile between its M and V phases
-  uint32_t pk[T::NKB][8];     // bf16 probabilities between a V phase and the next M phase
+  u32x4 pk[T::VC];            // bf16 probabilities between a V phase and the next M
+                              // phase, as the B operands of the V^T P^T k-chunks
+#pragma unroll
+  for (int kc = 0; kc < T::VC; ++kc) pk[kc] = u32x4{};
 
-  // M(k): scores of tile k, then P V of tile k-1.  The fragment reads run a
-  // few MFMAs ahead of their use so that the LDS latency stays hidden.
-  // U = k mod S (compile time), so every LDS slot offset is an immediate.
+  // M(k): scores of tile k, then P V of tile k-1, as one stream of MFMAs
+  // whose LDS fragment reads run LA MFMAs ahead (the V reads start while the
+  // score MFMAs still run).  U = k mod S (compile time), so every LDS slot
+  // offset is an immediate.
   auto m_phase = [&](auto U, int k) {
     constexpr int u = decltype(U)::value;
-    if (!group_b) {  // batch k
-      issue_k(integral_constant<int, (u + S - 1) % S>{}, k - 1 + S);
-      issue_v(integral_constant<int, (u + S - 2) % S>{}, k - 2 + S);
-    }
+    constexpr int ks = u;                // slot of K(k)
+    constexpr int vs = (u + S - 1) % S;  // slot of V(k-1)
+    issue_k(integral_constant<int, (u + S - 1) % S>{});  // batch k
+    issue_v(integral_constant<int, (u + S - 2) % S>{});
     __builtin_amdgcn_s_setprio(1);
-    if (k < n_tiles && !wave_skips(k)) {
-      constexpr int NQK = T::NKB * T::KC;  // MFMAs of the score tile
-      constexpr int LA = 8;                // reads in flight ahead
-      bf16x8 kf[NQK];
-      auto kld = [&](int i) {
-        const uint32_t a = kaddr[i % T::KC] + u * T::TILEB + (i / T::KC) * 32 * T::ROWB;
-        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
-      };
+    constexpr int NQK = T::NKB * T::KC;  // MFMAs of the score tile
+    constexpr int NPV = T::VC * T::NDB;  // MFMAs of the P V update
+    constexpr int LA = 8;                // MFMAs whose operands are read ahead
+    bf16x8 kf[NQK], vf[NPV];
+    auto kread = [&](int i) {  // i = kb * KC + kc
+      const uint32_t a = kaddr[i % T::KC] + ks * T::TILEB + (i / T::KC) * 32 * T::ROWB;
+      kf[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
+    };
+    auto vread = [&](int i) {  // i = kc * NDB + db
+      const uint32_t a = vaddr[i % T::NDB] + vs * T::TILEB + (i / T::NDB) * 16 * T::ROWB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a + 8 * T::ROWB));
+      vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto qk_mfma = [&](int i) {  // the first k-chunk starts from zero
+      st[i / T::KC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          kf[i], qf[i % T::KC], i % T::KC == 0 ? f32x16{} : st[i / T::KC], 0, 0, 0);
+    };
+    auto pv_mfma = [&](int i) {
+      const int kc = i / T::NDB, db = i % T::NDB;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], __builtin_bit_cast(bf16x8, pk[kc]),
+                                                       acc[db], 0, 0, 0);
+    };
+    // Both halves always run: a tile this wave does not see has all-zero
+    // probabilities (set by its V phase), and the scores of a tile it will
+    // not use are simply not read.  Skipping saves no time, since every wave
+    // waits at the same barriers.
+    // MFMA j < NQK is score MFMA j, else P V MFMA j - NQK; its operands are
+    // read before MFMA j - LA
+    auto read = [&](int j) { if (j < NQK) kread(j); else vread(j - NQK); };
 #pragma unroll
-      for (int i = 0; i < LA; ++i) kf[i] = kld(i);
+    for (int j = 0; j < LA; ++j) read(j);
 #pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb) st[kb] = f32x16{};
-#pragma unroll
-      for (int i = 0; i < NQK; ++i) {
-        if (i + LA < NQK) kf[i + LA] = kld(i + LA);
-        st[i / T::KC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i % T::KC], st[i / T::KC], 0, 0, 0);
-      }
-      // keep LA reads in flight: reads, then alternate one MFMA / one read
-      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
-#pragma unroll
-      for (int i = 0; i < NQK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i + LA < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+    for (int j = 0; j < NQK + NPV; ++j) {
+      if (j + LA < NQK + NPV) read(j + LA);
+      if (j < NQK) qk_mfma(j); else pv_mfma(j - NQK);
     }
-    if (k >= 1 && !wave_skips(k - 1)) {
-      constexpr int vs = (u + S - 1) % S;  // slot of V(k-1)
-      constexpr int NPV = T::VC * T::NDB;  // MFMAs of the P V update
-      constexpr int LA = 6;
-      bf16x8 vf[NPV];
-      auto vread = [&](int i) {  // i = kc * NDB + db
-        const uint32_t a = vaddr[i % T::NDB] + vs * T::TILEB + (i / T::NDB) * 16 * T::ROWB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a + 8 * T::ROWB));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
+    static_assert(LA <= NQK, "the read-ahead starts with score operands");
+    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
-      for (int i = 0; i < LA; ++i) vf[i] = vread(i);
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        if (i + LA < NPV) vf[i + LA] = vread(i + LA);
-        const int kc = i / T::NDB, db = i % T::NDB;
-        const int kb = kc >> 1, half = kc & 1;
-        u32x4 pw;
-        pw[0] = pk[kb][half * 4 + 0];
-        pw[1] = pk[kb][half * 4 + 1];
-        pw[2] = pk[kb][half * 4 + 2];
-        pw[3] = pk[kb][half * 4 + 3];
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], __builtin_bit_cast(bf16x8, pw),
-                                                         acc[db], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 1);
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (i + LA < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      }
+    for (int j = 0; j < NQK + NPV; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (j + LA < NQK)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      else if (j + LA < NQK + NPV)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_s_setprio(0);
     if (group_b) wait_vm<2 * T::LPW * (S - 2)>();
   };
 
-  // V(k): softmax of tile k (mask, lazy max, exponentials)
+  // exponentials of the tile against the reference max mref (base-2
+  // domain), packed to bf16 pairs; returns this lane's float32 partial row sum
+  auto exp_tile = [&](float mref) {
+    float rq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x0 = POS_SCALE ? fmaf(st[kb][2 * i], p.sl2, -mref) : st[kb][2 * i] - mref;
+        const float x1 = POS_SCALE ? fmaf(st[kb][2 * i + 1], p.sl2, -mref) : st[kb][2 * i + 1] - mref;
+        const float e0 = fast_exp2(x0), e1 = fast_exp2(x1);
+        pk[kb * 2 + (i >> 2)][i & 3] = pack_bf16x2(e0, e1);
+        rq[(2 * i) & 3] += e0;
+        rq[(2 * i + 1) & 3] += e1;
+      }
+    return (rq[0] + rq[1]) + (rq[2] + rq[3]);
+  };
+
+  // V(k): softmax of tile k (mask, exponentials, occasional max update)
   auto v_phase = [&](auto U, int k) {
-    constexpr int u = decltype(U)::value;
-    if (group_b) {  // batch k + 1
-      issue_k(integral_constant<int, u>{}, k + S);
-      issue_v(integral_constant<int, (u + S - 1) % S>{}, k - 1 + S);
-    }
+    (void)U;
     if (k < n_tiles && !wave_skips(k)) {
       const int j0 = (t_begin + k) * T::BN;
       if (!POS_SCALE) {
@@ -402,30 +427,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
             }
         }
       }
-      // online softmax with a lazily raised maximum: the stored max only moves
-      // when some row's max exceeds it by more than 2^8, so most tiles skip
-      // the accumulator rescale; probabilities stay <= 2^8, and the final
-      // division uses the sum taken at the same max, so the result is exact.
-      // row max as a tree (independent chains keep the VALU pipeline full)
-      float mq[4];
+      // fast path: against the stored max (m_run = -inf gives inf/NaN sums)
+      float ls = exp_tile(m_run);
+      if (__builtin_amdgcn_ballot_w64(!(ls <= kRaise)) != 0) {
+        // row max as a tree (independent chains keep the VALU pipeline full)
+        float mq[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mq[j] = fmaxf(st[0][4 * j], st[0][4 * j + 1]);
+        for (int j = 0; j < 4; ++j) mq[j] = fmaxf(st[0][4 * j], st[0][4 * j + 1]);
 #pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb)
+        for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (kb == 0 && (r & 3) < 2) continue;
-          mq[r >> 2] = fmaxf(mq[r >> 2], st[kb][r]);
+          for (int r = 0; r < 16; ++r) {
+            if (kb == 0 && (r & 3) < 2) continue;
+            mq[r >> 2] = fmaxf(mq[r >> 2], st[kb][r]);
+          }
+        float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+        {  // max with lane l ^ 32 (the same row) on the VALU
+          float a = mx, bb = mx;
+          // inline asm: the compiler folds a max of the builtin's two results away
+          asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(bb));
+          mx = fmaxf(a, bb);
         }
-      float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-      {  // max with lane l ^ 32 (the same row) on the VALU
-        float a = mx, bb = mx;
-        // inline asm: the compiler folds a max of the builtin's two results away
-        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(bb));
-        mx = fmaxf(a, bb);
-      }
-      if (POS_SCALE) mx *= p.sl2;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+        if (POS_SCALE) mx *= p.sl2;
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
@@ -434,46 +457,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
         m_run = m_new;
+        ls = exp_tile(m_run == kNegInf ? 0.f : m_run);  // row with nothing visible yet
       }
-      const float m_use = (m_run == kNegInf) ? 0.f : m_run;  // row with nothing visible yet
-      // exponentials in place, stage by stage, so that each stage is 32
-      // independent instructions
+      l_run += ls;
+    } else {
 #pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          st[kb][r] = POS_SCALE ? fmaf(st[kb][r], p.sl2, -m_use) : st[kb][r] - m_use;
-#pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[kb][r] = fast_exp2(st[kb][r]);
-#pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pk[kb][i] = pack_bf16x2(st[kb][2 * i], st[kb][2 * i + 1]);
-      // float32 row sum (the LSE must reproduce exp(S - LSE) to fp32), as a tree
-      float rq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) rq[r & 3] += st[kb][r];
-      l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
+      for (int kc = 0; kc < T::VC; ++kc) pk[kc] = u32x4{};
     }
     if (!group_b) wait_vm<2 * T::LPW * (S - 2)>();
   };
 
-  // prologue: K(0..S-2) and V(0..S-3) in LDS before the first barrier
-  unrolled_while<0, S - 1>([&](auto T_) { issue_k(T_, decltype(T_)::value); return true; });
-  unrolled_while<0, S - 2>([&](auto T_) { issue_v(T_, decltype(T_)::value); return true; });
+  // prologue: K(0..S-2) and V(0..S-3) in LDS before the first barrier; the
+  // slot of "V(-1)", which M(0) multiplies by zero probabilities, is zeroed
+  // (stale LDS could hold NaN)
+  for (int i = tid; i < T::TILEB / 16; i += kThreads)
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + (2 * S - 1) * T::TILEB + 16 * i) = u32x4{};
+  unrolled_while<0, S - 1>([&](auto T_) { issue_k(T_); return true; });
+  unrolled_while<0, S - 2>([&](auto T_) { issue_v(T_); return true; });
   wait_vm<0>();  // also completes the Q loads, once, outside the loop
 #pragma unroll
   for (int c = 0; c < T::KC; ++c) asm volatile("" ::"v"(qf[c]));
   lds_barrier();
-  if (group_b) {  // B's slot 0 (its "V(-1)"): batch 0
-    issue_k(integral_constant<int, S - 1>{}, S - 1);
-    issue_v(integral_constant<int, S - 2>{}, S - 2);
-    lds_barrier();
-  }
+  if (group_b) lds_barrier();  // B starts one slot behind A
   // S tiles per trip so that every LDS slot index is a compile-time constant;
   // the last step (k = n_tiles) only finishes P V of the last tile
   for (int k0 = 0;; k0 += S) {
