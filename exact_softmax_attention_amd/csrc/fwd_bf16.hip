@@ -44,6 +44,7 @@
 //   * Work groups are ordered heavy-first (last query tiles first) inside a
 //     head and remapped so that the tiles of one head share an XCD (and its
 //     L2), since they all stream the same K/V.
+#include <climits>
 #include <type_traits>
 
 #include "device_common.h"
@@ -258,10 +259,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     ++t;
   };
   // the next K tile into K slot SLOT, the next V tile into V slot SLOT
-  auto issue_k = [&](auto SLOT) {
+  auto issue_k = [&](auto SLOT) __attribute__((always_inline)) {
     issue(std::integral_constant<uint32_t, decltype(SLOT)::value * T::TILEB>{}, knext, kt, koff);
   };
-  auto issue_v = [&](auto SLOT) {
+  auto issue_v = [&](auto SLOT) __attribute__((always_inline)) {
     issue(std::integral_constant<uint32_t, (S + decltype(SLOT)::value) * T::TILEB>{}, vnext, vt, voff);
   };
   using std::integral_constant;
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     vaddr[db] = S * T::TILEB + vt_key * T::ROWB + ((piece ^ T::vswz(vt_key)) << 4) + 8 * (s16 & 1);
   }
 
-  auto wave_skips = [&](int k) {
+  auto wave_skips = [&](int k) __attribute__((always_inline)) {
     const int j0 = (t_begin + k) * T::BN;
     bool skip = qw0 >= p.Nq;
     if (p.causal && j0 > qw0 + kRowsPerWave - 1 + delta) skip = true;
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   // whose LDS fragment reads run LA MFMAs ahead (the V reads start while the
   // score MFMAs still run).  U = k mod S (compile time), so every LDS slot
   // offset is an immediate.
-  auto m_phase = [&](auto U, int k) {
+  auto m_phase = [&](auto U, int k) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;
     constexpr int ks = u;                // slot of K(k)
     constexpr int vs = (u + S - 1) % S;  // slot of V(k-1)
@@ -322,21 +323,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     constexpr int NPV = T::VC * T::NDB;  // MFMAs of the P V update
     constexpr int LA = 8;                // MFMAs whose operands are read ahead
     bf16x8 kf[NQK], vf[NPV];
-    auto kread = [&](int i) {  // i = kb * KC + kc
+    auto kread = [&](int i) __attribute__((always_inline)) {  // i = kb * KC + kc
       const uint32_t a = kaddr[i % T::KC] + ks * T::TILEB + (i / T::KC) * 32 * T::ROWB;
       kf[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
     };
-    auto vread = [&](int i) {  // i = kc * NDB + db
+    auto vread = [&](int i) __attribute__((always_inline)) {  // i = kc * NDB + db
       const uint32_t a = vaddr[i % T::NDB] + vs * T::TILEB + (i / T::NDB) * 16 * T::ROWB;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a + 8 * T::ROWB));
       vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto qk_mfma = [&](int i) {  // the first k-chunk starts from zero
+    auto qk_mfma = [&](int i) __attribute__((always_inline)) {  // the first k-chunk starts from zero
       st[i / T::KC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           kf[i], qf[i % T::KC], i % T::KC == 0 ? f32x16{} : st[i / T::KC], 0, 0, 0);
     };
-    auto pv_mfma = [&](int i) {
+    auto pv_mfma = [&](int i) __attribute__((always_inline)) {
       const int kc = i / T::NDB, db = i % T::NDB;
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], __builtin_bit_cast(bf16x8, pk[kc]),
                                                        acc[db], 0, 0, 0);
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     // waits at the same barriers.
     // MFMA j < NQK is score MFMA j, else P V MFMA j - NQK; its operands are
     // read before MFMA j - LA
-    auto read = [&](int j) { if (j < NQK) kread(j); else vread(j - NQK); };
+    auto read = [&](int j) __attribute__((always_inline)) { if (j < NQK) kread(j); else vread(j - NQK); };
 #pragma unroll
     for (int j = 0; j < LA; ++j) read(j);
 #pragma unroll
@@ -369,77 +370,83 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     if (group_b) wait_vm<2 * T::LPW * (S - 2)>();
   };
 
-  // exponentials of the tile against the reference max mref (base-2
-  // domain), packed to bf16 pairs; returns this lane's float32 partial row sum
-  auto exp_tile = [&](float mref) {
-    float rq[4] = {0.f, 0.f, 0.f, 0.f};
+  // Masking in place: key offset c (a compile-time constant per register, key
+  // = j0 + 4g + c) is hidden when c > hi (causal diagonal, key tail) or c < lo
+  // (window).  The compare/select pair is written in asm with the score tied
+  // to its own register, so that masked and unmasked tiles leave the scores
+  // where the MFMAs wrote them (the compiler otherwise copies them to merge
+  // the two paths).
+  auto mask_above = [&](int hi) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x0 = POS_SCALE ? fmaf(st[kb][2 * i], p.sl2, -mref) : st[kb][2 * i] - mref;
-        const float x1 = POS_SCALE ? fmaf(st[kb][2 * i + 1], p.sl2, -mref) : st[kb][2 * i + 1] - mref;
-        const float e0 = fast_exp2(x0), e1 = fast_exp2(x1);
-        pk[kb * 2 + (i >> 2)][i & 3] = pack_bf16x2(e0, e1);
-        rq[(2 * i) & 3] += e0;
-        rq[(2 * i + 1) & 3] += e1;
+      for (int r = 0; r < 16; ++r) {
+        const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+        asm("v_cmp_gt_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc"
+            : "+v"(st[kb][r]) : "n"(c), "v"(hi), "v"(kNegInf) : "vcc");
       }
+  };
+  auto mask_below = [&](int lo) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+        asm("v_cmp_lt_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc"
+            : "+v"(st[kb][r]) : "n"(c), "v"(lo), "v"(kNegInf) : "vcc");
+      }
+  };
+
+  // exponentials of the tile against the reference max mref (base-2
+  // domain), packed to bf16 pairs; returns this lane's float32 partial row sum
+  auto exp_tile = [&](float mref) __attribute__((always_inline)) {
+    float e[T::NKB][16];
+#pragma unroll
+    for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[kb][r] = fast_exp2(fmaf(st[kb][r], p.sl2, -mref));
+#pragma unroll
+    for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pk[kb * 2 + (i >> 2)][i & 3] = pack_bf16x2(e[kb][2 * i], e[kb][2 * i + 1]);
+    float rq[4] = {e[0][0], e[0][1], e[0][2], e[0][3]};
+#pragma unroll
+    for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) rq[r & 3] += e[kb][r];
     return (rq[0] + rq[1]) + (rq[2] + rq[3]);
   };
 
   // V(k): softmax of tile k (mask, exponentials, occasional max update)
-  auto v_phase = [&](auto U, int k) {
+  auto v_phase = [&](auto U, int k) __attribute__((always_inline)) {
     (void)U;
     if (k < n_tiles && !wave_skips(k)) {
       const int j0 = (t_begin + k) * T::BN;
-      if (!POS_SCALE) {
-#pragma unroll
-        for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) st[kb][r] *= p.sl2;
-      }
-      const bool need_mask = (j0 + T::BN > p.Nk) ||
-                             (p.causal && j0 + T::BN - 1 > qw0 + delta) ||
-                             (p.window > 0 && qw0 + kRowsPerWave - 1 + delta - j0 >= p.window);
-      if (need_mask) {
-        // visible keys of this lane's row, as offsets from the lane's first key
-        // (key = j0 + 4g + c with c a compile-time constant per register)
-        const int pos = qw0 + n + delta;
-        const int base = j0 + 4 * g;
+      const int pos = qw0 + n + delta;  // this lane's row position
+      const int base = j0 + 4 * g;      // key of offset 0 in this lane
+      if ((j0 + T::BN > p.Nk) || (p.causal && j0 + T::BN - 1 > qw0 + delta)) {
         int hi = p.Nk - 1 - base;
         if (p.causal) hi = min(hi, pos - base);
-        if (p.window > 0) {
-          const int lo = pos - p.window + 1 - base;
-#pragma unroll
-          for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-              if (c > hi || c < lo) st[kb][r] = kNegInf;
-            }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-              if (c > hi) st[kb][r] = kNegInf;
-            }
-        }
+        mask_above(hi);
       }
+      if (p.window > 0 && qw0 + kRowsPerWave - 1 + delta - j0 >= p.window)
+        mask_below(pos - p.window + 1 - base);
       // fast path: against the stored max (m_run = -inf gives inf/NaN sums)
       float ls = exp_tile(m_run);
       if (__builtin_amdgcn_ballot_w64(!(ls <= kRaise)) != 0) {
-        // row max as a tree (independent chains keep the VALU pipeline full)
+        // row max of the scaled scores as a tree
+        auto sv = [&](int kb, int r) __attribute__((always_inline)) {
+          return POS_SCALE ? st[kb][r] : st[kb][r] * p.sl2;
+        };
         float mq[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mq[j] = fmaxf(st[0][4 * j], st[0][4 * j + 1]);
+        for (int j = 0; j < 4; ++j) mq[j] = fmaxf(sv(0, 4 * j), sv(0, 4 * j + 1));
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             if (kb == 0 && (r & 3) < 2) continue;
-            mq[r >> 2] = fmaxf(mq[r >> 2], st[kb][r]);
+            mq[r >> 2] = fmaxf(mq[r >> 2], sv(kb, r));
           }
         float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
         {  // max with lane l ^ 32 (the same row) on the VALU
