@@ -2,6 +2,7 @@
 // gfx950 kernels.  Validation runs entirely on the host before any HIP call.
 #include "attn.h"
 
+#include <atomic>
 #include <climits>
 
 #include "launch.h"
@@ -50,6 +51,25 @@ int fwd_common(const void* q, const void* k, const void* v, void* out, float* ls
 }
 
 }  // namespace
+
+namespace attn {
+
+int device_cus() {
+  // per-device CU count, looked up once (racing first calls store the same value)
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
+}  // namespace attn
 
 extern "C" {
 

@@ -393,20 +393,6 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(cons
   }
 }
 
-int device_cus() {
-  // per-device CU count, looked up once (racing first calls store the same value)
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int cus = cached[dev].load(std::memory_order_relaxed);
-  if (cus == 0) {
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    cached[dev].store(cus, std::memory_order_relaxed);
-  }
-  return cus;
-}
 
 }  // namespace
 

@@ -190,339 +190,362 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   const int n = lane & 31;  // query row within the wave / MFMA column
   const int g = lane >> 5;  // k-half of the MFMA operands
 
-  const int item = xcd_remap(blockIdx.x, p.total);
-  const int bh = item / p.n_qtiles;
-  const int qt = p.n_qtiles - 1 - (item - bh * p.n_qtiles);
-  const int b = bh / p.Hq;
-  const int h = bh - b * p.Hq;
-  const int hk = h / p.group;
-  const int i0 = qt * kBM;
-  const int qw0 = i0 + wave * kRowsPerWave;
-  const int delta = p.Nk - p.Nq;
+  // Persistent schedule: one work group per CU walks a static list of work
+  // items (b, h, query tile).  Items are split over the XCDs in proportion to
+  // the work groups each XCD runs (work group w runs on XCD w % 8), in head
+  // order, so that the groups of one XCD share its L2 while they stream the
+  // same heads' K/V.  Within an XCD, round r hands items [r*Gx, r*Gx+Gx) to
+  // its Gx groups, alternating direction every round (heavy query tiles come
+  // first within a head, so the alternation evens out causal costs).
+  constexpr int kXcd = 8;
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % kXcd;
+  const int lw = blockIdx.x / kXcd;
+  int groups_before = 0;
+  for (int x = 0; x < xcd; ++x) groups_before += (G - x + kXcd - 1) / kXcd;
+  const int Gx = (G - xcd + kXcd - 1) / kXcd;
+  const int first = (int)((int64_t)p.total * groups_before / G);
+  const int n_items = (int)((int64_t)p.total * (groups_before + Gx) / G) - first;
+  for (int rnd = 0;; ++rnd) {
+    const int j = (rnd & 1) ? Gx - 1 - lw : lw;
+    const int idx = rnd * Gx + j;
+    if (idx >= n_items) break;
+    const int item = first + idx;
+    const int bh = item / p.n_qtiles;
+    const int qt = p.n_qtiles - 1 - (item - bh * p.n_qtiles);
+    const int b = bh / p.Hq;
+    const int h = bh - b * p.Hq;
+    const int hk = h / p.group;
+    const int i0 = qt * kBM;
+    const int qw0 = i0 + wave * kRowsPerWave;
+    const int delta = p.Nk - p.Nq;
 
-  int kv_end = p.Nk;
-  if (p.causal) kv_end = min(p.Nk, i0 + kBM + delta);
-  int kv_begin = 0;
-  if (p.window > 0) kv_begin = max(0, i0 + delta - p.window + 1);
-  const int t_begin = kv_begin / T::BN;
-  const int n_tiles = kv_end > kv_begin ? (kv_end + T::BN - 1) / T::BN - t_begin : 0;
+    int kv_end = p.Nk;
+    if (p.causal) kv_end = min(p.Nk, i0 + kBM + delta);
+    int kv_begin = 0;
+    if (p.window > 0) kv_begin = max(0, i0 + delta - p.window + 1);
+    const int t_begin = kv_begin / T::BN;
+    const int n_tiles = kv_end > kv_begin ? (kv_end + T::BN - 1) / T::BN - t_begin : 0;
 
-  // this wave's Q rows as the B operand of K Q^T (8 bf16 per k-chunk)
-  const int64_t q_row = (int64_t)p.Hq * D;
-  bf16x8 qf[T::KC];
-  {
-    const int row = min(qw0 + n, p.Nq - 1);  // rows past the end compute garbage, never stored
-    const uint16_t* qp = p.q + ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D + g * 8;
-#pragma unroll
-    for (int c = 0; c < T::KC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + c * 16);
-  }
-
-  // ---- loads into LDS.  Instruction i of a tile fills LDS bytes
-  // [1024 i, 1024 i + 1024) of the slot; lane L's 16 bytes land at 1024 i + 16 L,
-  // which is row r = (1024 i + 16 L) / ROWB, physical piece c; the lane
-  // fetches logical piece c ^ swizzle(r) of key row r.
-  const int64_t kv_row = (int64_t)p.Hkv * D;                 // elements between keys
-  const uint32_t kv_row_b = static_cast<uint32_t>(kv_row * 2);
-  const int64_t head_off = (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
-  const uint16_t* kbase = p.k + head_off;
-  const uint16_t* vbase = p.v + head_off;
-  int koff[T::LPW], voff[T::LPW];
-#pragma unroll
-  for (int j = 0; j < T::LPW; ++j) {
-    const int pos = (wave * T::LPW + j) * 1024 + lane * 16;
-    const int r = pos / T::ROWB;
-    const int c = (pos % T::ROWB) >> 4;
-    koff[j] = r * (int)kv_row_b + ((c ^ T::kswz(r)) << 4);
-    voff[j] = r * (int)kv_row_b + ((c ^ T::vswz(r)) << 4);
-  }
-  // Each wave issues the tiles of one kind in order (K(0), K(1), ... and
-  // V(0), V(1), ...), so a running byte address per kind is enough; the range
-  // of a tile is whole except for the last visible one, and zero past it.
-  const uint32_t lds_wave = lds0 + wave * T::LPW * 1024;
-  const uint32_t tile_b = (uint32_t)T::BN * kv_row_b;  // bytes of a whole tile's rows
-  uint32_t last_b = 0;  // bytes of the last visible tile: up to the end of key row Nk-1
-  if (n_tiles > 0) {
-    const int rows = p.Nk - (t_begin + n_tiles - 1) * T::BN;  // >= 1
-    last_b = rows >= T::BN ? tile_b : (uint32_t)(rows - 1) * kv_row_b + T::ROWB;
-  }
-  const uint8_t* knext = reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t_begin * tile_b;
-  const uint8_t* vnext = reinterpret_cast<const uint8_t*>(vbase) + (int64_t)t_begin * tile_b;
-  int kt = 0, vt = 0;  // index of the next tile of each kind
-  auto issue = [&](auto DST, const uint8_t*& next, int& t, const int (&off)[T::LPW]) {
-    constexpr uint32_t dst = decltype(DST)::value;
-    const uint32_t bytes = t < n_tiles - 1 ? tile_b : (t == n_tiles - 1 ? last_b : 0u);
-    const i32x4 rsrc = make_rsrc(next, bytes);
-    load_lds16<dst>(rsrc, off[0], lds_wave);
-    if constexpr (T::LPW > 1) load_lds16<dst + 1024>(rsrc, off[1], lds_wave);
-    static_assert(T::LPW <= 2, "load count per wave");
-    next += tile_b;
-    ++t;
-  };
-  // the next K tile into K slot SLOT, the next V tile into V slot SLOT
-  auto issue_k = [&](auto SLOT) __attribute__((always_inline)) {
-    issue(std::integral_constant<uint32_t, decltype(SLOT)::value * T::TILEB>{}, knext, kt, koff);
-  };
-  auto issue_v = [&](auto SLOT) __attribute__((always_inline)) {
-    issue(std::integral_constant<uint32_t, (S + decltype(SLOT)::value) * T::TILEB>{}, vnext, vt, voff);
-  };
-  using std::integral_constant;
-
-  // ---- LDS fragment offsets (bytes from the LDS base, per lane; slots and
-  // blocks are added as immediates)
-  // K: row n of the 32-key block, logical piece 2 kc + g
-  uint32_t kaddr[T::KC];
-#pragma unroll
-  for (int kc = 0; kc < T::KC; ++kc) kaddr[kc] = n * T::ROWB + (((2 * kc + g) ^ T::kswz(n)) << 4);
-  // V (transposing read): for MFMA k-chunk kc and feature block db, lane
-  // (group G = lane/16, s = lane%16) points at key kc*16 + (G/2)*4 + s/4
-  // (+8 for the second read) and features db*32 + 16*(G%2) + 4*(s%4).  The
-  // hardware hands lane 4r+c of each 16-lane group the 4 keys of source lanes
-  // r, r+4, r+8, r+12 at feature 4r+c, which is V^T in the operand layout, with
-  // lane group g holding keys {g*4..g*4+3, 8+g*4..8+g*4+3} of the chunk.
-  // The swizzle of a key row depends only on the key modulo 4.
-  const int G16 = lane >> 4, s16 = lane & 15;
-  const int vt_key = (G16 >> 1) * 4 + (s16 >> 2);
-  uint32_t vaddr[T::NDB];
-#pragma unroll
-  for (int db = 0; db < T::NDB; ++db) {
-    const int piece = db * 4 + 2 * (G16 & 1) + ((s16 & 3) >> 1);
-    vaddr[db] = S * T::TILEB + vt_key * T::ROWB + ((piece ^ T::vswz(vt_key)) << 4) + 8 * (s16 & 1);
-  }
-
-  auto wave_skips = [&](int k) __attribute__((always_inline)) {
-    const int j0 = (t_begin + k) * T::BN;
-    bool skip = qw0 >= p.Nq;
-    if (p.causal && j0 > qw0 + kRowsPerWave - 1 + delta) skip = true;
-    if (p.window > 0 && j0 + T::BN - 1 < qw0 + delta - p.window + 1) skip = true;
-    return skip;
-  };
-
-  float m_run = kNegInf;  // running row max (base-2 domain), same in lanes n and n+32
-  float l_run = 0.f;      // running row sum over this lane's keys
-  f32x16 acc[T::NDB];
-#pragma unroll
-  for (int db = 0; db < T::NDB; ++db) acc[db] = f32x16{};
-  f32x16 st[T::NKB];          // scores of the tile between its M and V phases
-  u32x4 pk[T::VC];            // bf16 probabilities between a V phase and the next M
-                              // phase, as the B operands of the V^T P^T k-chunks
-#pragma unroll
-  for (int kc = 0; kc < T::VC; ++kc) pk[kc] = u32x4{};
-
-  // M(k): scores of tile k, then P V of tile k-1, as one stream of MFMAs
-  // whose LDS fragment reads run LA MFMAs ahead (the V reads start while the
-  // score MFMAs still run).  U = k mod S (compile time), so every LDS slot
-  // offset is an immediate.
-  auto m_phase = [&](auto U, int k) __attribute__((always_inline)) {
-    constexpr int u = decltype(U)::value;
-    constexpr int ks = u;                // slot of K(k)
-    constexpr int vs = (u + S - 1) % S;  // slot of V(k-1)
-    issue_k(integral_constant<int, (u + S - 1) % S>{});  // batch k
-    issue_v(integral_constant<int, (u + S - 2) % S>{});
-    __builtin_amdgcn_s_setprio(1);
-    constexpr int NQK = T::NKB * T::KC;  // MFMAs of the score tile
-    constexpr int NPV = T::VC * T::NDB;  // MFMAs of the P V update
-    constexpr int LA = 8;                // MFMAs whose operands are read ahead
-    bf16x8 kf[NQK], vf[NPV];
-    auto kread = [&](int i) __attribute__((always_inline)) {  // i = kb * KC + kc
-      const uint32_t a = kaddr[i % T::KC] + ks * T::TILEB + (i / T::KC) * 32 * T::ROWB;
-      kf[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
-    };
-    auto vread = [&](int i) __attribute__((always_inline)) {  // i = kc * NDB + db
-      const uint32_t a = vaddr[i % T::NDB] + vs * T::TILEB + (i / T::NDB) * 16 * T::ROWB;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a + 8 * T::ROWB));
-      vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    auto qk_mfma = [&](int i) __attribute__((always_inline)) {  // the first k-chunk starts from zero
-      st[i / T::KC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          kf[i], qf[i % T::KC], i % T::KC == 0 ? f32x16{} : st[i / T::KC], 0, 0, 0);
-    };
-    auto pv_mfma = [&](int i) __attribute__((always_inline)) {
-      const int kc = i / T::NDB, db = i % T::NDB;
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], __builtin_bit_cast(bf16x8, pk[kc]),
-                                                       acc[db], 0, 0, 0);
-    };
-    // Both halves always run: a tile this wave does not see has all-zero
-    // probabilities (set by its V phase), and the scores of a tile it will
-    // not use are simply not read.  Skipping saves no time, since every wave
-    // waits at the same barriers.
-    // MFMA j < NQK is score MFMA j, else P V MFMA j - NQK; its operands are
-    // read before MFMA j - LA
-    auto read = [&](int j) __attribute__((always_inline)) { if (j < NQK) kread(j); else vread(j - NQK); };
-#pragma unroll
-    for (int j = 0; j < LA; ++j) read(j);
-#pragma unroll
-    for (int j = 0; j < NQK + NPV; ++j) {
-      if (j + LA < NQK + NPV) read(j + LA);
-      if (j < NQK) qk_mfma(j); else pv_mfma(j - NQK);
+    // this wave's Q rows as the B operand of K Q^T (8 bf16 per k-chunk)
+    const int64_t q_row = (int64_t)p.Hq * D;
+    bf16x8 qf[T::KC];
+    {
+      const int row = min(qw0 + n, p.Nq - 1);  // rows past the end compute garbage, never stored
+      const uint16_t* qp = p.q + ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D + g * 8;
+  #pragma unroll
+      for (int c = 0; c < T::KC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + c * 16);
     }
-    static_assert(LA <= NQK, "the read-ahead starts with score operands");
-    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
-#pragma unroll
-    for (int j = 0; j < NQK + NPV; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (j + LA < NQK)
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      else if (j + LA < NQK + NPV)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+
+    // ---- loads into LDS.  Instruction i of a tile fills LDS bytes
+    // [1024 i, 1024 i + 1024) of the slot; lane L's 16 bytes land at 1024 i + 16 L,
+    // which is row r = (1024 i + 16 L) / ROWB, physical piece c; the lane
+    // fetches logical piece c ^ swizzle(r) of key row r.
+    const int64_t kv_row = (int64_t)p.Hkv * D;                 // elements between keys
+    const uint32_t kv_row_b = static_cast<uint32_t>(kv_row * 2);
+    const int64_t head_off = (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
+    const uint16_t* kbase = p.k + head_off;
+    const uint16_t* vbase = p.v + head_off;
+    int koff[T::LPW], voff[T::LPW];
+  #pragma unroll
+    for (int j = 0; j < T::LPW; ++j) {
+      const int pos = (wave * T::LPW + j) * 1024 + lane * 16;
+      const int r = pos / T::ROWB;
+      const int c = (pos % T::ROWB) >> 4;
+      koff[j] = r * (int)kv_row_b + ((c ^ T::kswz(r)) << 4);
+      voff[j] = r * (int)kv_row_b + ((c ^ T::vswz(r)) << 4);
     }
-    __builtin_amdgcn_s_setprio(0);
-    if (group_b) wait_vm<2 * T::LPW * (S - 2)>();
-  };
+    // Each wave issues the tiles of one kind in order (K(0), K(1), ... and
+    // V(0), V(1), ...), so a running byte address per kind is enough; the range
+    // of a tile is whole except for the last visible one, and zero past it.
+    const uint32_t lds_wave = lds0 + wave * T::LPW * 1024;
+    const uint32_t tile_b = (uint32_t)T::BN * kv_row_b;  // bytes of a whole tile's rows
+    uint32_t last_b = 0;  // bytes of the last visible tile: up to the end of key row Nk-1
+    if (n_tiles > 0) {
+      const int rows = p.Nk - (t_begin + n_tiles - 1) * T::BN;  // >= 1
+      last_b = rows >= T::BN ? tile_b : (uint32_t)(rows - 1) * kv_row_b + T::ROWB;
+    }
+    const uint8_t* knext = reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t_begin * tile_b;
+    const uint8_t* vnext = reinterpret_cast<const uint8_t*>(vbase) + (int64_t)t_begin * tile_b;
+    int kt = 0, vt = 0;  // index of the next tile of each kind
+    auto issue = [&](auto DST, const uint8_t*& next, int& t, const int (&off)[T::LPW]) {
+      constexpr uint32_t dst = decltype(DST)::value;
+      const uint32_t bytes = t < n_tiles - 1 ? tile_b : (t == n_tiles - 1 ? last_b : 0u);
+      const i32x4 rsrc = make_rsrc(next, bytes);
+      load_lds16<dst>(rsrc, off[0], lds_wave);
+      if constexpr (T::LPW > 1) load_lds16<dst + 1024>(rsrc, off[1], lds_wave);
+      static_assert(T::LPW <= 2, "load count per wave");
+      next += tile_b;
+      ++t;
+    };
+    // the next K tile into K slot SLOT, the next V tile into V slot SLOT
+    auto issue_k = [&](auto SLOT) __attribute__((always_inline)) {
+      issue(std::integral_constant<uint32_t, decltype(SLOT)::value * T::TILEB>{}, knext, kt, koff);
+    };
+    auto issue_v = [&](auto SLOT) __attribute__((always_inline)) {
+      issue(std::integral_constant<uint32_t, (S + decltype(SLOT)::value) * T::TILEB>{}, vnext, vt, voff);
+    };
+    using std::integral_constant;
 
-  // Masking in place: key offset c (a compile-time constant per register, key
-  // = j0 + 4g + c) is hidden when c > hi (causal diagonal, key tail) or c < lo
-  // (window).  The compare/select pair is written in asm with the score tied
-  // to its own register, so that masked and unmasked tiles leave the scores
-  // where the MFMAs wrote them (the compiler otherwise copies them to merge
-  // the two paths).
-  auto mask_above = [&](int hi) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-        asm("v_cmp_gt_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc"
-            : "+v"(st[kb][r]) : "n"(c), "v"(hi), "v"(kNegInf) : "vcc");
-      }
-  };
-  auto mask_below = [&](int lo) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-        asm("v_cmp_lt_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc"
-            : "+v"(st[kb][r]) : "n"(c), "v"(lo), "v"(kNegInf) : "vcc");
-      }
-  };
+    // ---- LDS fragment offsets (bytes from the LDS base, per lane; slots and
+    // blocks are added as immediates)
+    // K: row n of the 32-key block, logical piece 2 kc + g
+    uint32_t kaddr[T::KC];
+  #pragma unroll
+    for (int kc = 0; kc < T::KC; ++kc) kaddr[kc] = n * T::ROWB + (((2 * kc + g) ^ T::kswz(n)) << 4);
+    // V (transposing read): for MFMA k-chunk kc and feature block db, lane
+    // (group G = lane/16, s = lane%16) points at key kc*16 + (G/2)*4 + s/4
+    // (+8 for the second read) and features db*32 + 16*(G%2) + 4*(s%4).  The
+    // hardware hands lane 4r+c of each 16-lane group the 4 keys of source lanes
+    // r, r+4, r+8, r+12 at feature 4r+c, which is V^T in the operand layout, with
+    // lane group g holding keys {g*4..g*4+3, 8+g*4..8+g*4+3} of the chunk.
+    // The swizzle of a key row depends only on the key modulo 4.
+    const int G16 = lane >> 4, s16 = lane & 15;
+    const int vt_key = (G16 >> 1) * 4 + (s16 >> 2);
+    uint32_t vaddr[T::NDB];
+  #pragma unroll
+    for (int db = 0; db < T::NDB; ++db) {
+      const int piece = db * 4 + 2 * (G16 & 1) + ((s16 & 3) >> 1);
+      vaddr[db] = S * T::TILEB + vt_key * T::ROWB + ((piece ^ T::vswz(vt_key)) << 4) + 8 * (s16 & 1);
+    }
 
-  // exponentials of the tile against the reference max mref (base-2
-  // domain), packed to bf16 pairs; returns this lane's float32 partial row sum
-  auto exp_tile = [&](float mref) __attribute__((always_inline)) {
-    float e[T::NKB][16];
-#pragma unroll
-    for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) e[kb][r] = fast_exp2(fmaf(st[kb][r], p.sl2, -mref));
-#pragma unroll
-    for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pk[kb * 2 + (i >> 2)][i & 3] = pack_bf16x2(e[kb][2 * i], e[kb][2 * i + 1]);
-    float rq[4] = {e[0][0], e[0][1], e[0][2], e[0][3]};
-#pragma unroll
-    for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-      for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) rq[r & 3] += e[kb][r];
-    return (rq[0] + rq[1]) + (rq[2] + rq[3]);
-  };
-
-  // V(k): softmax of tile k (mask, exponentials, occasional max update)
-  auto v_phase = [&](auto U, int k) __attribute__((always_inline)) {
-    (void)U;
-    if (k < n_tiles && !wave_skips(k)) {
+    auto wave_skips = [&](int k) __attribute__((always_inline)) {
       const int j0 = (t_begin + k) * T::BN;
-      const int pos = qw0 + n + delta;  // this lane's row position
-      const int base = j0 + 4 * g;      // key of offset 0 in this lane
-      if ((j0 + T::BN > p.Nk) || (p.causal && j0 + T::BN - 1 > qw0 + delta)) {
-        int hi = p.Nk - 1 - base;
-        if (p.causal) hi = min(hi, pos - base);
-        mask_above(hi);
+      bool skip = qw0 >= p.Nq;
+      if (p.causal && j0 > qw0 + kRowsPerWave - 1 + delta) skip = true;
+      if (p.window > 0 && j0 + T::BN - 1 < qw0 + delta - p.window + 1) skip = true;
+      return skip;
+    };
+
+    float m_run = kNegInf;  // running row max (base-2 domain), same in lanes n and n+32
+    float l_run = 0.f;      // running row sum over this lane's keys
+    f32x16 acc[T::NDB];
+  #pragma unroll
+    for (int db = 0; db < T::NDB; ++db) acc[db] = f32x16{};
+    f32x16 st[T::NKB];          // scores of the tile between its M and V phases
+    u32x4 pk[T::VC];            // bf16 probabilities between a V phase and the next M
+                                // phase, as the B operands of the V^T P^T k-chunks
+  #pragma unroll
+    for (int kc = 0; kc < T::VC; ++kc) pk[kc] = u32x4{};
+
+    // M(k): scores of tile k, then P V of tile k-1, as one stream of MFMAs
+    // whose LDS fragment reads run LA MFMAs ahead (the V reads start while the
+    // score MFMAs still run).  U = k mod S (compile time), so every LDS slot
+    // offset is an immediate.
+    auto m_phase = [&](auto U, int k) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      constexpr int ks = u;                // slot of K(k)
+      constexpr int vs = (u + S - 1) % S;  // slot of V(k-1)
+      issue_k(integral_constant<int, (u + S - 1) % S>{});  // batch k
+      issue_v(integral_constant<int, (u + S - 2) % S>{});
+      __builtin_amdgcn_s_setprio(1);
+      constexpr int NQK = T::NKB * T::KC;  // MFMAs of the score tile
+      constexpr int NPV = T::VC * T::NDB;  // MFMAs of the P V update
+      constexpr int LA = 8;                // MFMAs whose operands are read ahead
+      bf16x8 kf[NQK], vf[NPV];
+      auto kread = [&](int i) __attribute__((always_inline)) {  // i = kb * KC + kc
+        const uint32_t a = kaddr[i % T::KC] + ks * T::TILEB + (i / T::KC) * 32 * T::ROWB;
+        kf[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
+      };
+      auto vread = [&](int i) __attribute__((always_inline)) {  // i = kc * NDB + db
+        const uint32_t a = vaddr[i % T::NDB] + vs * T::TILEB + (i / T::NDB) * 16 * T::ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a + 8 * T::ROWB));
+        vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      auto qk_mfma = [&](int i) __attribute__((always_inline)) {  // the first k-chunk starts from zero
+        st[i / T::KC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            kf[i], qf[i % T::KC], i % T::KC == 0 ? f32x16{} : st[i / T::KC], 0, 0, 0);
+      };
+      auto pv_mfma = [&](int i) __attribute__((always_inline)) {
+        const int kc = i / T::NDB, db = i % T::NDB;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], __builtin_bit_cast(bf16x8, pk[kc]),
+                                                         acc[db], 0, 0, 0);
+      };
+      // Both halves always run: a tile this wave does not see has all-zero
+      // probabilities (set by its V phase), and the scores of a tile it will
+      // not use are simply not read.  Skipping saves no time, since every wave
+      // waits at the same barriers.
+      // MFMA j < NQK is score MFMA j, else P V MFMA j - NQK; its operands are
+      // read before MFMA j - LA
+      auto read = [&](int j) __attribute__((always_inline)) { if (j < NQK) kread(j); else vread(j - NQK); };
+  #pragma unroll
+      for (int j = 0; j < LA; ++j) read(j);
+  #pragma unroll
+      for (int j = 0; j < NQK + NPV; ++j) {
+        if (j + LA < NQK + NPV) read(j + LA);
+        if (j < NQK) qk_mfma(j); else pv_mfma(j - NQK);
       }
-      if (p.window > 0 && qw0 + kRowsPerWave - 1 + delta - j0 >= p.window)
-        mask_below(pos - p.window + 1 - base);
-      // fast path: against the stored max (m_run = -inf gives inf/NaN sums)
-      float ls = exp_tile(m_run);
-      if (__builtin_amdgcn_ballot_w64(!(ls <= kRaise)) != 0) {
-        // row max of the scaled scores as a tree
-        auto sv = [&](int kb, int r) __attribute__((always_inline)) {
-          return POS_SCALE ? st[kb][r] : st[kb][r] * p.sl2;
-        };
-        float mq[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mq[j] = fmaxf(sv(0, 4 * j), sv(0, 4 * j + 1));
-#pragma unroll
-        for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if (kb == 0 && (r & 3) < 2) continue;
-            mq[r >> 2] = fmaxf(mq[r >> 2], sv(kb, r));
-          }
-        float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-        {  // max with lane l ^ 32 (the same row) on the VALU
-          float a = mx, bb = mx;
-          // inline asm: the compiler folds a max of the builtin's two results away
-          asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(bb));
-          mx = fmaxf(a, bb);
+      static_assert(LA <= NQK, "the read-ahead starts with score operands");
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+  #pragma unroll
+      for (int j = 0; j < NQK + NPV; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (j + LA < NQK)
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        else if (j + LA < NQK + NPV)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (group_b) wait_vm<2 * T::LPW * (S - 2)>();
+    };
+
+    // Masking in place: key offset c (a compile-time constant per register, key
+    // = j0 + 4g + c) is hidden when c > hi (causal diagonal, key tail) or c < lo
+    // (window).  The compare/select pair is written in asm with the score tied
+    // to its own register, so that masked and unmasked tiles leave the scores
+    // where the MFMAs wrote them (the compiler otherwise copies them to merge
+    // the two paths).
+    auto mask_above = [&](int hi) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          asm("v_cmp_gt_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc"
+              : "+v"(st[kb][r]) : "n"(c), "v"(hi), "v"(kNegInf) : "vcc");
         }
-        if (POS_SCALE) mx *= p.sl2;
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-        m_run = m_new;
-        ls = exp_tile(m_run == kNegInf ? 0.f : m_run);  // row with nothing visible yet
+    };
+    auto mask_below = [&](int lo) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          asm("v_cmp_lt_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc"
+              : "+v"(st[kb][r]) : "n"(c), "v"(lo), "v"(kNegInf) : "vcc");
+        }
+    };
+
+    // exponentials of the tile against the reference max mref (base-2
+    // domain), packed to bf16 pairs; returns this lane's float32 partial row sum
+    auto exp_tile = [&](float mref) __attribute__((always_inline)) {
+      float e[T::NKB][16];
+  #pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) e[kb][r] = fast_exp2(fmaf(st[kb][r], p.sl2, -mref));
+  #pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) pk[kb * 2 + (i >> 2)][i & 3] = pack_bf16x2(e[kb][2 * i], e[kb][2 * i + 1]);
+      float rq[4] = {e[0][0], e[0][1], e[0][2], e[0][3]};
+  #pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+  #pragma unroll
+        for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) rq[r & 3] += e[kb][r];
+      return (rq[0] + rq[1]) + (rq[2] + rq[3]);
+    };
+
+    // V(k): softmax of tile k (mask, exponentials, occasional max update)
+    auto v_phase = [&](auto U, int k) __attribute__((always_inline)) {
+      (void)U;
+      if (k < n_tiles && !wave_skips(k)) {
+        const int j0 = (t_begin + k) * T::BN;
+        const int pos = qw0 + n + delta;  // this lane's row position
+        const int base = j0 + 4 * g;      // key of offset 0 in this lane
+        if ((j0 + T::BN > p.Nk) || (p.causal && j0 + T::BN - 1 > qw0 + delta)) {
+          int hi = p.Nk - 1 - base;
+          if (p.causal) hi = min(hi, pos - base);
+          mask_above(hi);
+        }
+        if (p.window > 0 && qw0 + kRowsPerWave - 1 + delta - j0 >= p.window)
+          mask_below(pos - p.window + 1 - base);
+        // fast path: against the stored max (m_run = -inf gives inf/NaN sums)
+        float ls = exp_tile(m_run);
+        if (__builtin_amdgcn_ballot_w64(!(ls <= kRaise)) != 0) {
+          // row max of the scaled scores as a tree
+          auto sv = [&](int kb, int r) __attribute__((always_inline)) {
+            return POS_SCALE ? st[kb][r] : st[kb][r] * p.sl2;
+          };
+          float mq[4];
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) mq[j] = fmaxf(sv(0, 4 * j), sv(0, 4 * j + 1));
+  #pragma unroll
+          for (int kb = 0; kb < T::NKB; ++kb)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              if (kb == 0 && (r & 3) < 2) continue;
+              mq[r >> 2] = fmaxf(mq[r >> 2], sv(kb, r));
+            }
+          float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+          {  // max with lane l ^ 32 (the same row) on the VALU
+            float a = mx, bb = mx;
+            // inline asm: the compiler folds a max of the builtin's two results away
+            asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(bb));
+            mx = fmaxf(a, bb);
+          }
+          if (POS_SCALE) mx *= p.sl2;
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+          l_run *= alpha;
+  #pragma unroll
+          for (int db = 0; db < T::NDB; ++db)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+          m_run = m_new;
+          ls = exp_tile(m_run == kNegInf ? 0.f : m_run);  // row with nothing visible yet
+        }
+        l_run += ls;
+      } else {
+  #pragma unroll
+        for (int kc = 0; kc < T::VC; ++kc) pk[kc] = u32x4{};
       }
-      l_run += ls;
-    } else {
-#pragma unroll
-      for (int kc = 0; kc < T::VC; ++kc) pk[kc] = u32x4{};
+      if (!group_b) wait_vm<2 * T::LPW * (S - 2)>();
+    };
+
+    // prologue: K(0..S-2) and V(0..S-3) in LDS before the first barrier; the
+    // slot of "V(-1)", which M(0) multiplies by zero probabilities, is zeroed
+    // (stale LDS could hold NaN)
+    for (int i = tid; i < T::TILEB / 16; i += kThreads)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + (2 * S - 1) * T::TILEB + 16 * i) = u32x4{};
+    unrolled_while<0, S - 1>([&](auto T_) { issue_k(T_); return true; });
+    unrolled_while<0, S - 2>([&](auto T_) { issue_v(T_); return true; });
+    wait_vm<0>();  // also completes the Q loads, once, outside the loop
+  #pragma unroll
+    for (int c = 0; c < T::KC; ++c) asm volatile("" ::"v"(qf[c]));
+    lds_barrier();
+    if (group_b) lds_barrier();  // B starts one slot behind A
+    // S tiles per trip so that every LDS slot index is a compile-time constant;
+    // the last step (k = n_tiles) only finishes P V of the last tile
+    for (int k0 = 0;; k0 += S) {
+      const bool more = unrolled_while<0, S>([&](auto U) {
+        const int k = k0 + decltype(U)::value;
+        m_phase(U, k);
+        lds_barrier();
+        v_phase(U, k);
+        lds_barrier();
+        return k < n_tiles;
+      });
+      if (!more) break;
     }
-    if (!group_b) wait_vm<2 * T::LPW * (S - 2)>();
-  };
+    if (!group_b) lds_barrier();  // A's extra barrier matches B's first one
+    wait_vm<0>();  // loads past the last tile still land in LDS: drain them
+    // every wave's loads have landed before the next item's loads start
+    __syncthreads();
 
-  // prologue: K(0..S-2) and V(0..S-3) in LDS before the first barrier; the
-  // slot of "V(-1)", which M(0) multiplies by zero probabilities, is zeroed
-  // (stale LDS could hold NaN)
-  for (int i = tid; i < T::TILEB / 16; i += kThreads)
-    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + (2 * S - 1) * T::TILEB + 16 * i) = u32x4{};
-  unrolled_while<0, S - 1>([&](auto T_) { issue_k(T_); return true; });
-  unrolled_while<0, S - 2>([&](auto T_) { issue_v(T_); return true; });
-  wait_vm<0>();  // also completes the Q loads, once, outside the loop
-#pragma unroll
-  for (int c = 0; c < T::KC; ++c) asm volatile("" ::"v"(qf[c]));
-  lds_barrier();
-  if (group_b) lds_barrier();  // B starts one slot behind A
-  // S tiles per trip so that every LDS slot index is a compile-time constant;
-  // the last step (k = n_tiles) only finishes P V of the last tile
-  for (int k0 = 0;; k0 += S) {
-    const bool more = unrolled_while<0, S>([&](auto U) {
-      const int k = k0 + decltype(U)::value;
-      m_phase(U, k);
-      lds_barrier();
-      v_phase(U, k);
-      lds_barrier();
-      return k < n_tiles;
-    });
-    if (!more) break;
-  }
-  if (!group_b) lds_barrier();  // A's extra barrier matches B's first one
-  wait_vm<0>();  // loads past the last tile still land in LDS: drain them
-
-  // epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
-  float la = l_run, lb = l_run;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(la), "+v"(lb));
-  const float l_tot = la + lb;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int row = qw0 + n;
-  if (row < p.Nq) {
-    uint16_t* op = p.o + ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D;
-#pragma unroll
-    for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = db * 32 + r4 * 8 + g * 4;
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[db][r4 * 4 + 0] * inv, acc[db][r4 * 4 + 1] * inv);
-        w[1] = pack_bf16x2(acc[db][r4 * 4 + 2] * inv, acc[db][r4 * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d) = w;
-      }
-    if (p.lse != nullptr && g == 0)
-      p.lse[((int64_t)b * p.Hq + h) * p.Nq + row] =
-          l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    // epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
+    float la = l_run, lb = l_run;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(la), "+v"(lb));
+    const float l_tot = la + lb;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int row = qw0 + n;
+    if (row < p.Nq) {
+      uint16_t* op = p.o + ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D;
+  #pragma unroll
+      for (int db = 0; db < T::NDB; ++db)
+  #pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = db * 32 + r4 * 8 + g * 4;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[db][r4 * 4 + 0] * inv, acc[db][r4 * 4 + 1] * inv);
+          w[1] = pack_bf16x2(acc[db][r4 * 4 + 2] * inv, acc[db][r4 * 4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + d) = w;
+        }
+      if (p.lse != nullptr && g == 0)
+        p.lse[((int64_t)b * p.Hq + h) * p.Nq + row] =
+            l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
   }
 }
 
@@ -550,7 +573,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.total = (int)fwd_bf16_grid(a.B, a.Hq, a.Nq);
   p.sl2 = a.scale * kLog2e;
   if (p.total == 0) return hipSuccess;
-  const dim3 grid(p.total), block(kThreads);
+  // one persistent work group per CU (the LDS ring admits one per CU)
+  const dim3 grid(p.total < device_cus() ? p.total : device_cus()), block(kThreads);
   const bool pos = a.scale > 0.f;
   if (a.d == 128) {
     if (pos)

@@ -6,6 +6,9 @@
 
 namespace attn {
 
+// Compute units of the current device (looked up once per device).
+int device_cus();
+
 struct FwdArgs {
   const void* q;
   const void* k;
