@@ -158,10 +158,12 @@ __device__ __forceinline__ bool unrolled_while(F&& f) {
 // K(m-1) and V(m-2), which were last read in slot 2m-1.  Each wave issues its
 // share of batch m at the start of its own M(m): group A in slot 2m, group B
 // in slot 2m+1 (the MFMA phase leaves the wave's issue slots idle).  Batch m
-// is first read in slot 2m+2S-2, so every wave waits for its own loads of
-// batch m at the end of slot 2m+2S-3 (the S-2 later batches may stay in
-// flight), before the barrier.  Loads of tiles past the last one read nothing
-// and fill free slots.
+// is first read in slot 2m+2S-3, where group A's V(m+S-2) reads ahead the
+// first operands of its M(m+S-1), so every wave waits for its own loads of
+// batch m at the end of slot 2m+2S-4, before the barrier: group A at the end
+// of an M phase (S-2 later batches may stay in flight), group B at the end
+// of a V phase (S-3 later batches).  Loads of tiles past the last one read
+// nothing and fill free slots.
 //
 // Softmax: the exponentials are first taken against the stored row maximum.
 // The online softmax is exact for any reference value that keeps the terms
@@ -328,6 +330,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   #pragma unroll
     for (int kc = 0; kc < T::VC; ++kc) pk[kc] = u32x4{};
 
+    constexpr int NQK = T::NKB * T::KC;  // MFMAs of the score tile
+    constexpr int NPV = T::VC * T::NDB;  // MFMAs of the P V update
+    constexpr int LA = 8;                // MFMAs whose operands are read ahead
+    static_assert(LA <= NQK, "the read-ahead starts with score operands");
+    // K fragment i (= kb * KC + kc) of the tile in K slot `slot`
+    auto kfrag = [&](int slot, int i) __attribute__((always_inline)) {
+      const uint32_t a = kaddr[i % T::KC] + slot * T::TILEB + (i / T::KC) * 32 * T::ROWB;
+      return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
+    };
+    bf16x8 kpre[LA];  // read ahead across the barrier into the next M phase
+
     // M(k): scores of tile k, then P V of tile k-1, as one stream of MFMAs
     // whose LDS fragment reads run LA MFMAs ahead (the V reads start while the
     // score MFMAs still run).  U = k mod S (compile time), so every LDS slot
@@ -339,14 +352,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       issue_k(integral_constant<int, (u + S - 1) % S>{});  // batch k
       issue_v(integral_constant<int, (u + S - 2) % S>{});
       __builtin_amdgcn_s_setprio(1);
-      constexpr int NQK = T::NKB * T::KC;  // MFMAs of the score tile
-      constexpr int NPV = T::VC * T::NDB;  // MFMAs of the P V update
-      constexpr int LA = 8;                // MFMAs whose operands are read ahead
       bf16x8 kf[NQK], vf[NPV];
-      auto kread = [&](int i) __attribute__((always_inline)) {  // i = kb * KC + kc
-        const uint32_t a = kaddr[i % T::KC] + ks * T::TILEB + (i / T::KC) * 32 * T::ROWB;
-        kf[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
-      };
+      auto kread = [&](int i) __attribute__((always_inline)) { kf[i] = kfrag(ks, i); };
       auto vread = [&](int i) __attribute__((always_inline)) {  // i = kc * NDB + db
         const uint32_t a = vaddr[i % T::NDB] + vs * T::TILEB + (i / T::NDB) * 16 * T::ROWB;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a));
@@ -367,17 +374,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       // not use are simply not read.  Skipping saves no time, since every wave
       // waits at the same barriers.
       // MFMA j < NQK is score MFMA j, else P V MFMA j - NQK; its operands are
-      // read before MFMA j - LA
+      // read before MFMA j - LA.  The first LA were read at the end of this
+      // wave's previous V phase (kpre), so the matrix pipe starts at once.
       auto read = [&](int j) __attribute__((always_inline)) { if (j < NQK) kread(j); else vread(j - NQK); };
   #pragma unroll
-      for (int j = 0; j < LA; ++j) read(j);
+      for (int j = 0; j < LA; ++j) kf[j] = kpre[j];
   #pragma unroll
       for (int j = 0; j < NQK + NPV; ++j) {
         if (j + LA < NQK + NPV) read(j + LA);
         if (j < NQK) qk_mfma(j); else pv_mfma(j - NQK);
       }
-      static_assert(LA <= NQK, "the read-ahead starts with score operands");
-      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
   #pragma unroll
       for (int j = 0; j < NQK + NPV; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_s_setprio(0);
-      if (group_b) wait_vm<2 * T::LPW * (S - 2)>();
+      if (!group_b) wait_vm<2 * T::LPW * (S - 2)>();
     };
 
     // Masking in place: key offset c (a compile-time constant per register, key
@@ -491,7 +497,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   #pragma unroll
         for (int kc = 0; kc < T::VC; ++kc) pk[kc] = u32x4{};
       }
-      if (!group_b) wait_vm<2 * T::LPW * (S - 2)>();
+      // the first LA score operands of M(k+1): K(k+1) is complete (see the
+      // load schedule) and its slot is not reloaded before M(k+2)
+  #pragma unroll
+      for (int j = 0; j < LA; ++j) kpre[j] = kfrag((decltype(U)::value + 1) % S, j);
+      if (group_b) wait_vm<2 * T::LPW * (S - 3)>();
     };
 
     // prologue: K(0..S-2) and V(0..S-3) in LDS before the first barrier; the
@@ -506,6 +516,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     for (int c = 0; c < T::KC; ++c) asm volatile("" ::"v"(qf[c]));
     lds_barrier();
     if (group_b) lds_barrier();  // B starts one slot behind A
+  #pragma unroll
+    for (int j = 0; j < LA; ++j) kpre[j] = kfrag(0, j);
     // S tiles per trip so that every LDS slot index is a compile-time constant;
     // the last step (k = n_tiles) only finishes P V of the last tile
     for (int k0 = 0;; k0 += S) {
