@@ -94,6 +94,7 @@ struct Params {
   uint16_t* o;
   float* lse;
   int Hq, Hkv, group, Nq, Nk, causal, window, n_qtiles, total;
+  int pairing;  // work units are pairs of query tiles (see the schedule)
   float sl2;  // scale * log2(e): scores are kept in the base-2 domain
 };
 
@@ -193,12 +194,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   const int g = lane >> 5;  // k-half of the MFMA operands
 
   // Persistent schedule: one work group per CU walks a static list of work
-  // items (b, h, query tile).  Items are split over the XCDs in proportion to
-  // the work groups each XCD runs (work group w runs on XCD w % 8), in head
-  // order, so that the groups of one XCD share its L2 while they stream the
-  // same heads' K/V.  Within an XCD, round r hands items [r*Gx, r*Gx+Gx) to
-  // its Gx groups, alternating direction every round (heavy query tiles come
-  // first within a head, so the alternation evens out causal costs).
+  // units.  With pairing, a unit is two query tiles of one head, the j-th
+  // heaviest and the j-th lightest (under a causal mask all such pairs cost
+  // the same), processed heavy first; otherwise a unit is one query tile.
+  // Units are ordered by head and split over the XCDs in proportion to the
+  // work groups each XCD runs (work group w runs on XCD w % 8); an XCD's Gx
+  // groups take its units round-robin.  So the groups of one XCD start their
+  // units together, on the same few heads, and stream the same K/V through
+  // their shared L2.
   constexpr int kXcd = 8;
   const int G = gridDim.x;
   const int xcd = blockIdx.x % kXcd;
@@ -206,15 +209,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   int groups_before = 0;
   for (int x = 0; x < xcd; ++x) groups_before += (G - x + kXcd - 1) / kXcd;
   const int Gx = (G - xcd + kXcd - 1) / kXcd;
-  const int first = (int)((int64_t)p.total * groups_before / G);
-  const int n_items = (int)((int64_t)p.total * (groups_before + Gx) / G) - first;
-  for (int rnd = 0;; ++rnd) {
-    const int j = (rnd & 1) ? Gx - 1 - lw : lw;
-    const int idx = rnd * Gx + j;
-    if (idx >= n_items) break;
-    const int item = first + idx;
-    const int bh = item / p.n_qtiles;
-    const int qt = p.n_qtiles - 1 - (item - bh * p.n_qtiles);
+  const int nq = p.n_qtiles;
+  const int per_head = p.pairing ? (nq + 1) / 2 : nq;
+  const int units = p.total / nq * per_head;
+  const int first = (int)((int64_t)units * groups_before / G);
+  const int last = (int)((int64_t)units * (groups_before + Gx) / G);
+  for (int unit = first + lw; unit < last; unit += Gx)
+  for (int e = 0; e < 2; ++e) {
+    const int bh = unit / per_head;
+    const int j = unit - bh * per_head;
+    if (e == 1 && (!p.pairing || j == nq - 1 - j)) break;
+    const int qt = e == 0 ? nq - 1 - j : j;  // heavy first
     const int b = bh / p.Hq;
     const int h = bh - b * p.Hq;
     const int hk = h / p.group;
@@ -585,8 +590,13 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.total = (int)fwd_bf16_grid(a.B, a.Hq, a.Nq);
   p.sl2 = a.scale * kLog2e;
   if (p.total == 0) return hipSuccess;
-  // one persistent work group per CU (the LDS ring admits one per CU)
-  const dim3 grid(p.total < device_cus() ? p.total : device_cus()), block(kThreads);
+  // one persistent work group per CU (the LDS ring admits one per CU); pair
+  // query tiles when there are enough pairs to fill the CUs
+  const int cus = device_cus();
+  const long long pairs = (long long)(p.total / p.n_qtiles) * ((p.n_qtiles + 1) / 2);
+  p.pairing = pairs >= cus ? 1 : 0;
+  const long long units = p.pairing ? pairs : p.total;
+  const dim3 grid(units < cus ? (int)units : cus), block(kThreads);
   const bool pos = a.scale > 0.f;
   if (a.d == 128) {
     if (pos)

@@ -190,3 +190,21 @@ def test_swa_causal_32k():
     ow, lw = attn_fwd(qd, kd, vd, causal=True, window=cfg.Nk, scale=cfg.scale)
     assert torch.equal(oc, ow) and torch.equal(lc, lw)
     assert not torch.equal(out, oc)
+
+
+def test_paired_schedule_odd_query_tiles():
+    """33 query tiles per head (an odd count) and enough heads that the
+    persistent schedule pairs heavy and light query tiles of a head; the
+    middle tile runs alone.  Rows of the first, middle, last and a ragged
+    tile are checked against the oracle on heads across the KV groups."""
+    B, Hq, Hkv, N, d = 1, 16, 4, 33 * 256 - 100, 64
+    q, k, v = workloads.make_dense(B, Hq, Hkv, N, N, d, 81)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    out, lse = _run("bf16", q, k, v, True, 0, scale)
+    assert torch.isfinite(out).all().item()
+    rows = np.array(sorted({0, 1, 255, 256, 16 * 256 - 1, 16 * 256, 16 * 256 + 17, 17 * 256 - 1,
+                            17 * 256, 31 * 256 + 5, N - 1, N - 2} | set(range(N - 40, N, 7))))
+    heads = [(0, 0), (0, 3), (0, 4), (0, 9), (0, 15)]
+    ref = oracle.attention(q, k, v, scale, True, 0, heads=heads, rows=rows)
+    for (b, h), (O, L) in ref.items():
+        check(out[b, rows, h], O, lse[b, h, rows], L, "bf16", f"paired b{b} h{h}")
