@@ -220,6 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     const int j = unit - bh * per_head;
     if (e == 1 && (!p.pairing || j == nq - 1 - j)) break;
     const int qt = e == 0 ? nq - 1 - j : j;  // heavy first
+    __syncthreads();  // the previous item's O staging is done with the ring
     const int b = bh / p.Hq;
     const int h = bh - b * p.Hq;
     const int hk = h / p.group;
@@ -541,28 +542,45 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     // every wave's loads have landed before the next item's loads start
     __syncthreads();
 
-    // epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
+    // epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2.  O goes
+    // through this wave's own LDS region (the ring is idle now), so that it
+    // leaves as whole 256-byte rows (16 lanes x 16 bytes) rather than as
+    // 8-byte pieces scattered over 32 rows.  The row pitch of 2D + 16 bytes
+    // spreads the scattered writes over the banks.
     float la = l_run, lb = l_run;
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(la), "+v"(lb));
     const float l_tot = la + lb;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int row = qw0 + n;
-    if (row < p.Nq) {
-      uint16_t* op = p.o + ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D;
+    constexpr int OPITCH = T::ROWB + 16;  // bytes per staged row
+    static_assert(kWaves * kRowsPerWave * OPITCH <= T::LDS_BYTES, "O staging fits the ring");
+    const uint32_t ostage = wave * kRowsPerWave * OPITCH;
   #pragma unroll
-      for (int db = 0; db < T::NDB; ++db)
+    for (int db = 0; db < T::NDB; ++db)
   #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d = db * 32 + r4 * 8 + g * 4;
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[db][r4 * 4 + 0] * inv, acc[db][r4 * 4 + 1] * inv);
-          w[1] = pack_bf16x2(acc[db][r4 * 4 + 2] * inv, acc[db][r4 * 4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + d) = w;
-        }
-      if (p.lse != nullptr && g == 0)
-        p.lse[((int64_t)b * p.Hq + h) * p.Nq + row] =
-            l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + r4 * 8 + g * 4;
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][r4 * 4 + 0] * inv, acc[db][r4 * 4 + 1] * inv);
+        w[1] = pack_bf16x2(acc[db][r4 * 4 + 2] * inv, acc[db][r4 * 4 + 3] * inv);
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds + ostage + n * OPITCH + 2 * d) = w;
+      }
+    {
+      constexpr int LPR = T::ROWB / 16;     // lanes per row
+      constexpr int RPI = 64 / LPR;         // rows per store instruction
+      const int rr = lane / LPR, cc = lane % LPR;
+  #pragma unroll
+      for (int i = 0; i < kRowsPerWave / RPI; ++i) {
+        const int r = i * RPI + rr;
+        const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            lds + ostage + r * OPITCH + 16 * cc);
+        if (qw0 + r < p.Nq)
+          *reinterpret_cast<u32x4*>(p.o + ((int64_t)b * p.Nq + qw0 + r) * q_row + (int64_t)h * D + 8 * cc) = w;
+      }
     }
+    const int row = qw0 + n;
+    if (row < p.Nq && p.lse != nullptr && g == 0)
+      p.lse[((int64_t)b * p.Hq + h) * p.Nq + row] =
+          l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
 }
 
