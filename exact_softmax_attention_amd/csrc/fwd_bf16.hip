@@ -44,6 +44,7 @@
 //   * Work groups are ordered heavy-first (last query tiles first) inside a
 //     head and remapped so that the tiles of one head share an XCD (and its
 //     L2), since they all stream the same K/V.
+#include <atomic>
 #include <climits>
 #include <type_traits>
 
@@ -94,9 +95,18 @@ struct Params {
   uint16_t* o;
   float* lse;
   int Hq, Hkv, group, Nq, Nk, causal, window, n_qtiles, total;
+  int slot;     // this launch's slot of scheduling counters
   int pairing;  // work units are pairs of query tiles (see the schedule)
   float sl2;  // scale * log2(e): scores are kept in the base-2 domain
 };
+
+// Scheduling counters of the persistent kernel: slot s holds one item counter
+// per XCD and a count of finished work groups.  Launches take slots in turn,
+// so that launches in flight on different streams do not share counters; the
+// last work group of a launch returns its slot to zero.
+constexpr int kXcds = 8;  // XCDs of the device; work group w runs on XCD w % 8
+constexpr int kSchedSlots = 64;
+__device__ int g_sched[kSchedSlots * (kXcds + 1)];
 
 // Buffer resource for raw (unswizzled) 32-bit addressing: loads at byte
 // offsets >= bytes return zero and touch no memory.
@@ -193,19 +203,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   const int n = lane & 31;  // query row within the wave / MFMA column
   const int g = lane >> 5;  // k-half of the MFMA operands
 
-  // Persistent schedule: one work group per CU walks a static list of work
-  // units.  With pairing, a unit is two query tiles of one head, the j-th
-  // heaviest and the j-th lightest (under a causal mask all such pairs cost
-  // the same), processed heavy first; otherwise a unit is one query tile.
-  // Units are ordered by head and split over the XCDs in proportion to the
-  // work groups each XCD runs (work group w runs on XCD w % 8); an XCD's Gx
-  // groups take its units round-robin.  So the groups of one XCD start their
-  // units together, on the same few heads, and stream the same K/V through
-  // their shared L2.
-  constexpr int kXcd = 8;
+  // Persistent schedule: one work group per CU takes work units from a queue
+  // until it is empty.  With pairing, a unit is two query tiles of one head,
+  // the j-th heaviest and the j-th lightest (under a causal mask all such
+  // pairs cost the same), processed heavy first; otherwise a unit is one
+  // query tile.  Units are ordered by head, the costliest first within a head,
+  // and split over the XCDs in proportion to the work groups each XCD runs
+  // (work group w runs on XCD w % 8); each XCD hands out its range through its
+  // own counter.  So the groups of an XCD work on the same few heads at a time
+  // (their K/V stream through the XCD's L2), and the cheap units, taken last,
+  // even out the finishing times whatever the cost of each unit.
+  constexpr int kXcd = kXcds;
+  __shared__ int s_unit;  // the next unit, broadcast from thread 0
   const int G = gridDim.x;
   const int xcd = blockIdx.x % kXcd;
-  const int lw = blockIdx.x / kXcd;
   int groups_before = 0;
   for (int x = 0; x < xcd; ++x) groups_before += (G - x + kXcd - 1) / kXcd;
   const int Gx = (G - xcd + kXcd - 1) / kXcd;
@@ -214,13 +225,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   const int units = p.total / nq * per_head;
   const int first = (int)((int64_t)units * groups_before / G);
   const int last = (int)((int64_t)units * (groups_before + Gx) / G);
-  for (int unit = first + lw; unit < last; unit += Gx)
+  int* const ctr = g_sched + p.slot * (kXcd + 1);  // [xcd counters..., finished groups]
+  if (tid == 0) s_unit = first + atomicAdd(ctr + xcd, 1);
+  __syncthreads();
+  for (int unit = s_unit; unit < last;) {
+  int grabbed = 0;  // the unit after this one, in flight meanwhile
+  if (tid == 0) grabbed = atomicAdd(ctr + xcd, 1);
+  const int bh = unit / per_head;
+  // pairs: the middle (costliest under a window) first; tiles: heavy first
+  const int j = per_head - 1 - (unit - bh * per_head);
   for (int e = 0; e < 2; ++e) {
-    const int bh = unit / per_head;
-    const int j = unit - bh * per_head;
     if (e == 1 && (!p.pairing || j == nq - 1 - j)) break;
-    const int qt = e == 0 ? nq - 1 - j : j;  // heavy first
-    __syncthreads();  // the previous item's O staging is done with the ring
+    const int qt = p.pairing ? (e == 0 ? nq - 1 - j : j) : nq - 1 - (per_head - 1 - j);
+    if (e == 1) __syncthreads();  // the first tile's O staging is done with the ring
     const int b = bh / p.Hq;
     const int h = bh - b * p.Hq;
     const int hk = h / p.group;
@@ -582,6 +599,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       p.lse[((int64_t)b * p.Hq + h) * p.Nq + row] =
           l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
+  // the O staging is done with the ring before the next unit's loads
+  if (tid == 0) s_unit = first + grabbed;
+  __syncthreads();
+  unit = s_unit;
+  }
+  // The last group to finish returns this launch's counters to zero for the
+  // next launch that uses the same slot (every group's final take precedes
+  // its count of finished groups).
+  if (tid == 0) {
+    __threadfence();
+    if (atomicAdd(ctr + kXcd, 1) == G - 1) {
+      for (int x = 0; x <= kXcd; ++x) atomicExch(ctr + x, 0);
+    }
+  }
 }
 
 }  // namespace
@@ -608,8 +639,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.total = (int)fwd_bf16_grid(a.B, a.Hq, a.Nq);
   p.sl2 = a.scale * kLog2e;
   if (p.total == 0) return hipSuccess;
-  // one persistent work group per CU (the LDS ring admits one per CU); pair
-  // query tiles when there are enough pairs to fill the CUs
+  // one persistent work group per CU (the LDS ring admits one per CU)
+  static std::atomic<unsigned> launches{0};
+  p.slot = (int)(launches.fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
+  // pair query tiles when there are enough pairs to fill the CUs
   const int cus = device_cus();
   const long long pairs = (long long)(p.total / p.n_qtiles) * ((p.n_qtiles + 1) / 2);
   p.pairing = pairs >= cus ? 1 : 0;

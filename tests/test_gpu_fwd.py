@@ -208,3 +208,40 @@ def test_paired_schedule_odd_query_tiles():
     ref = oracle.attention(q, k, v, scale, True, 0, heads=heads, rows=rows)
     for (b, h), (O, L) in ref.items():
         check(out[b, rows, h], O, lse[b, h, rows], L, "bf16", f"paired b{b} h{h}")
+
+
+def test_persistent_queue_reuse_and_streams():
+    """The persistent kernel takes its work from counters that live across
+    launches (a ring of 64 slots, each returned to zero by its launch).  Many
+    launches in a row, of shapes that alternate between the paired and the
+    single-tile schedules, and launches in flight on two streams at once must
+    all reproduce the result of a lone launch bit for bit."""
+    shapes = [
+        (4, 32, 8, 8192, 8192, 128, True, 0),   # paired query tiles
+        (1, 4, 2, 700, 700, 64, True, 0),       # single tiles
+        (2, 8, 8, 1500, 1500, 128, False, 0),
+    ]
+    inputs, refs = [], []
+    for i, (B, Hq, Hkv, Nq, Nk, d, causal, w) in enumerate(shapes):
+        q, k, v = workloads.make_dense(B, Hq, Hkv, Nq, Nk, d, 90 + i)
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        inputs.append((qd, kd, vd, causal, w))
+        refs.append(attn_fwd(qd, kd, vd, causal=causal, window=w))
+    torch.cuda.synchronize()
+    for it in range(70):
+        s = it % len(shapes)
+        qd, kd, vd, causal, w = inputs[s]
+        out, lse = attn_fwd(qd, kd, vd, causal=causal, window=w)
+        torch.cuda.synchronize()
+        assert torch.equal(out, refs[s][0]) and torch.equal(lse, refs[s][1]), f"launch {it}"
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(4):
+        results = []
+        for s, st in enumerate(streams):
+            qd, kd, vd, causal, w = inputs[s]
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                results.append(attn_fwd(qd, kd, vd, causal=causal, window=w))
+        torch.cuda.synchronize()
+        for s, (out, lse) in enumerate(results):
+            assert torch.equal(out, refs[s][0]) and torch.equal(lse, refs[s][1]), f"stream {s} rep {rep}"
