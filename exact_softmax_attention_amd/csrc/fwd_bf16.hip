@@ -314,10 +314,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
 
     // ---- LDS fragment offsets (bytes from the LDS base, per lane; slots and
     // blocks are added as immediates)
-    // K: row n of the 32-key block, logical piece 2 kc + g
-    uint32_t kaddr[T::KC];
-  #pragma unroll
-    for (int kc = 0; kc < T::KC; ++kc) kaddr[kc] = n * T::ROWB + (((2 * kc + g) ^ T::kswz(n)) << 4);
+    // K: row n of the 32-key block, logical piece 2 kc + g, which sits at
+    // piece (2kc + g) ^ swz(n) = (g ^ swz(n)) ^ 2kc: the fragment of k-chunk kc
+    // is at kfrag0 ^ (kc << 5) (the row term has no bits there)
+    const uint32_t kfrag0 = n * T::ROWB + ((g ^ T::kswz(n)) << 4);
     // V (transposing read): for MFMA k-chunk kc and feature block db, lane
     // (group G = lane/16, s = lane%16) points at key kc*16 + (G/2)*4 + s/4
     // (+8 for the second read) and features db*32 + 16*(G%2) + 4*(s%4).  The
@@ -359,10 +359,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     static_assert(LA <= NQK, "the read-ahead starts with score operands");
     // K fragment i (= kb * KC + kc) of the tile in K slot `slot`
     auto kfrag = [&](int slot, int i) __attribute__((always_inline)) {
-      const uint32_t a = kaddr[i % T::KC] + slot * T::TILEB + (i / T::KC) * 32 * T::ROWB;
+      const uint32_t a = (kfrag0 ^ ((i % T::KC) << 5)) + slot * T::TILEB + (i / T::KC) * 32 * T::ROWB;
       return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
     };
-    bf16x8 kpre[LA];  // read ahead across the barrier into the next M phase
+    // score operands read ahead across the barrier, at the end of the V
+    // phase (which has slack); 12 of 16 is what the registers allow
+    constexpr int NPRE = NQK < 12 ? NQK : 12;
+    bf16x8 kpre[NPRE];
 
     // M(k): scores of tile k, then P V of tile k-1, as one stream of MFMAs
     // whose LDS fragment reads run LA MFMAs ahead (the V reads start while the
@@ -397,22 +400,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       // not use are simply not read.  Skipping saves no time, since every wave
       // waits at the same barriers.
       // MFMA j < NQK is score MFMA j, else P V MFMA j - NQK; its operands are
-      // read before MFMA j - LA.  The first LA were read at the end of this
-      // wave's previous V phase (kpre), so the matrix pipe starts at once.
+      // read before MFMA j - LA, except the first NPRE, which were read at the
+      // end of this wave's previous V phase (kpre): the matrix pipe starts at
+      // once and the score MFMAs do not wait on LDS.
       auto read = [&](int j) __attribute__((always_inline)) { if (j < NQK) kread(j); else vread(j - NQK); };
   #pragma unroll
-      for (int j = 0; j < LA; ++j) kf[j] = kpre[j];
+      for (int j = 0; j < NPRE; ++j) kf[j] = kpre[j];
   #pragma unroll
       for (int j = 0; j < NQK + NPV; ++j) {
-        if (j + LA < NQK + NPV) read(j + LA);
+        if (j + LA < NQK + NPV && j + LA >= NPRE) read(j + LA);
         if (j < NQK) qk_mfma(j); else pv_mfma(j - NQK);
       }
   #pragma unroll
       for (int j = 0; j < NQK + NPV; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (j + LA < NQK)
+        if (j + LA < NQK && j + LA >= NPRE)
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        else if (j + LA < NQK + NPV)
+        else if (j + LA >= NQK && j + LA < NQK + NPV)
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_s_setprio(0);
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       // the first LA score operands of M(k+1): K(k+1) is complete (see the
       // load schedule) and its slot is not reloaded before M(k+2)
   #pragma unroll
-      for (int j = 0; j < LA; ++j) kpre[j] = kfrag((decltype(U)::value + 1) % S, j);
+      for (int j = 0; j < NPRE; ++j) kpre[j] = kfrag((decltype(U)::value + 1) % S, j);
       if (group_b) wait_vm<2 * T::LPW * (S - 3)>();
     };
 
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     lds_barrier();
     if (group_b) lds_barrier();  // B starts one slot behind A
   #pragma unroll
-    for (int j = 0; j < LA; ++j) kpre[j] = kfrag(0, j);
+    for (int j = 0; j < NPRE; ++j) kpre[j] = kfrag(0, j);
     // S tiles per trip so that every LDS slot index is a compile-time constant;
     // the last step (k = n_tiles) only finishes P V of the last tile
     for (int k0 = 0;; k0 += S) {
