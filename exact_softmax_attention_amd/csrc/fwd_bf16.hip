@@ -148,6 +148,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Barrier that leaves this wave's LDS reads in flight: for reads of a slot
+// that no wave rewrites before this wave has consumed them.  The empty asm
+// statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier_reads_in_flight() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int floordiv(int a, int b) {  // b > 0
+  const int q = a / b;
+  return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+
 template <int I, int N, typename F>
 __device__ __forceinline__ bool unrolled_while(F&& f) {
   if constexpr (I < N) {
@@ -334,6 +348,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       vaddr[db] = S * T::TILEB + vt_key * T::ROWB + ((piece ^ T::vswz(vt_key)) << 4) + 8 * (s16 & 1);
     }
 
+    // Tiles [kf0, kf1) are visible to every row of this wave and need no mask.
+    int kf0 = 0, kf1 = 0;
+    if (qw0 < p.Nq) {
+      int hi = min(n_tiles, p.Nk / T::BN - t_begin);  // before the key tail
+      if (p.causal) hi = min(hi, floordiv(qw0 + delta + 1, T::BN) - t_begin);
+      int lo = 0;
+      if (p.window > 0) lo = max(0, -floordiv(p.window - qw0 - kRowsPerWave - delta, T::BN) - t_begin);
+      kf0 = lo;
+      kf1 = max(lo, hi);
+    }
     auto wave_skips = [&](int k) __attribute__((always_inline)) {
       const int j0 = (t_begin + k) * T::BN;
       bool skip = qw0 >= p.Nq;
@@ -371,13 +395,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     // whose LDS fragment reads run LA MFMAs ahead (the V reads start while the
     // score MFMAs still run).  U = k mod S (compile time), so every LDS slot
     // offset is an immediate.
-    auto m_phase = [&](auto U, int k) __attribute__((always_inline)) {
+    auto m_phase = [&](auto U, int k, int& vcase) __attribute__((always_inline)) {
       constexpr int u = decltype(U)::value;
+      // case of tile k for the V phase (scalar work, done here where the
+      // issue slots are idle): 0 no mask, 1 masked, 2 not visible
+      vcase = (unsigned)(k - kf0) < (unsigned)(kf1 - kf0) ? 0 : (k < n_tiles && !wave_skips(k)) ? 1 : 2;
+      asm volatile("" : "+s"(vcase));
       constexpr int ks = u;                // slot of K(k)
       constexpr int vs = (u + S - 1) % S;  // slot of V(k-1)
       issue_k(integral_constant<int, (u + S - 1) % S>{});  // batch k
       issue_v(integral_constant<int, (u + S - 2) % S>{});
-      __builtin_amdgcn_s_setprio(1);
       bf16x8 kf[NQK], vf[NPV];
       auto kread = [&](int i) __attribute__((always_inline)) { kf[i] = kfrag(ks, i); };
       auto vread = [&](int i) __attribute__((always_inline)) {  // i = kc * NDB + db
@@ -419,7 +446,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
         else if (j + LA >= NQK && j + LA < NQK + NPV)
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_s_setprio(0);
       if (!group_b) wait_vm<2 * T::LPW * (S - 2)>();
     };
 
@@ -471,19 +497,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     };
 
     // V(k): softmax of tile k (mask, exponentials, occasional max update)
-    auto v_phase = [&](auto U, int k) __attribute__((always_inline)) {
+    auto v_phase = [&](auto U, int k, int vcase) __attribute__((always_inline)) {
       (void)U;
-      if (k < n_tiles && !wave_skips(k)) {
-        const int j0 = (t_begin + k) * T::BN;
-        const int pos = qw0 + n + delta;  // this lane's row position
-        const int base = j0 + 4 * g;      // key of offset 0 in this lane
-        if ((j0 + T::BN > p.Nk) || (p.causal && j0 + T::BN - 1 > qw0 + delta)) {
-          int hi = p.Nk - 1 - base;
-          if (p.causal) hi = min(hi, pos - base);
-          mask_above(hi);
+      if (vcase != 2) {
+        if (vcase == 1) {
+          const int j0 = (t_begin + k) * T::BN;
+          const int pos = qw0 + n + delta;  // this lane's row position
+          const int base = j0 + 4 * g;      // key of offset 0 in this lane
+          if ((j0 + T::BN > p.Nk) || (p.causal && j0 + T::BN - 1 > qw0 + delta)) {
+            int hi = p.Nk - 1 - base;
+            if (p.causal) hi = min(hi, pos - base);
+            mask_above(hi);
+          }
+          if (p.window > 0 && qw0 + kRowsPerWave - 1 + delta - j0 >= p.window)
+            mask_below(pos - p.window + 1 - base);
         }
-        if (p.window > 0 && qw0 + kRowsPerWave - 1 + delta - j0 >= p.window)
-          mask_below(pos - p.window + 1 - base);
         // fast path: against the stored max (m_run = -inf gives inf/NaN sums)
         float ls = exp_tile(m_run);
         if (__builtin_amdgcn_ballot_w64(!(ls <= kRaise)) != 0) {
@@ -550,10 +578,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     for (int k0 = 0;; k0 += S) {
       const bool more = unrolled_while<0, S>([&](auto U) {
         const int k = k0 + decltype(U)::value;
-        m_phase(U, k);
+        int vcase;
+        m_phase(U, k, vcase);
         lds_barrier();
-        v_phase(U, k);
-        lds_barrier();
+        v_phase(U, k, vcase);
+        lds_barrier_reads_in_flight();
         return k < n_tiles;
       });
       if (!more) break;
