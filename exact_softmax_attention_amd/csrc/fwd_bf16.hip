@@ -317,6 +317,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       next += tile_b;
       ++t;
     };
+    auto rsrc_of = [&](const uint8_t* next, int t) __attribute__((always_inline)) {
+      const uint32_t bytes = t < n_tiles - 1 ? tile_b : (t == n_tiles - 1 ? last_b : 0u);
+      return make_rsrc(next, bytes);
+    };
     // the next K tile into K slot SLOT, the next V tile into V slot SLOT
     auto issue_k = [&](auto SLOT) __attribute__((always_inline)) {
       issue(std::integral_constant<uint32_t, decltype(SLOT)::value * T::TILEB>{}, knext, kt, koff);
@@ -387,8 +391,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
     };
     // score operands read ahead across the barrier, at the end of the V
-    // phase (which has slack); 12 of 16 is what the registers allow
-    constexpr int NPRE = NQK < 12 ? NQK : 12;
+    // phase (deeper read-ahead measured no faster and costs 4 registers per
+    // fragment)
+    constexpr int NPRE = NQK < 8 ? NQK : 8;
     bf16x8 kpre[NPRE];
 
     // M(k): scores of tile k, then P V of tile k-1, as one stream of MFMAs
@@ -399,12 +404,39 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       constexpr int u = decltype(U)::value;
       // case of tile k for the V phase (scalar work, done here where the
       // issue slots are idle): 0 no mask, 1 masked, 2 not visible
-      vcase = (unsigned)(k - kf0) < (unsigned)(kf1 - kf0) ? 0 : (k < n_tiles && !wave_skips(k)) ? 1 : 2;
-      asm volatile("" : "+s"(vcase));
       constexpr int ks = u;                // slot of K(k)
       constexpr int vs = (u + S - 1) % S;  // slot of V(k-1)
-      issue_k(integral_constant<int, (u + S - 1) % S>{});  // batch k
-      issue_v(integral_constant<int, (u + S - 2) % S>{});
+      constexpr uint32_t kdst = ((u + S - 1) % S) * T::TILEB;        // batch k
+      constexpr uint32_t vdst = (S + (u + S - 2) % S) * T::TILEB;
+      i32x4 rk, rv;
+      // The loads of batch k and the scalar work, one piece after each of the
+      // first MFMAs: issued in one block they held up the matrix pipe, since
+      // a wave issues in order.
+      static_assert(T::LPW == 1 || T::LPW == 2, "load count per wave");
+      auto piece = [&](int j) __attribute__((always_inline)) {
+        if (j == 0) {
+          rk = rsrc_of(knext, kt);
+          load_lds16<kdst>(rk, koff[0], lds_wave);
+        }
+        if (j == 1) {
+          if constexpr (T::LPW > 1) load_lds16<kdst + 1024>(rk, koff[1], lds_wave);
+          knext += tile_b;
+          ++kt;
+        }
+        if (j == 2) {
+          rv = rsrc_of(vnext, vt);
+          load_lds16<vdst>(rv, voff[0], lds_wave);
+        }
+        if (j == 3) {
+          if constexpr (T::LPW > 1) load_lds16<vdst + 1024>(rv, voff[1], lds_wave);
+          vnext += tile_b;
+          ++vt;
+        }
+        if (j == 4) {
+          vcase = (unsigned)(k - kf0) < (unsigned)(kf1 - kf0) ? 0 : (k < n_tiles && !wave_skips(k)) ? 1 : 2;
+          asm volatile("" : "+s"(vcase));
+        }
+      };
       bf16x8 kf[NQK], vf[NPV];
       auto kread = [&](int i) __attribute__((always_inline)) { kf[i] = kfrag(ks, i); };
       auto vread = [&](int i) __attribute__((always_inline)) {  // i = kc * NDB + db
@@ -437,6 +469,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       for (int j = 0; j < NQK + NPV; ++j) {
         if (j + LA < NQK + NPV && j + LA >= NPRE) read(j + LA);
         if (j < NQK) qk_mfma(j); else pv_mfma(j - NQK);
+        if (j < 5) piece(j);
       }
   #pragma unroll
       for (int j = 0; j < NQK + NPV; ++j) {
