@@ -16,12 +16,14 @@ Modules:
                sharing, log-sum-exp, and the paged-cache decode oracle
   online     - the online softmax and the tiled recurrence (pages' algorithm)
   brute      - pure-Python loops with math.fsum, for n <= 16
+  backward   - fp64 gradients dQ, dK, dV of the plain definition
 
 Every function is pinned by the ``-m "not gpu"`` tests in ``tests/`` against
 the pages' printed values, closed forms and invariants.
 """
 from .attention import attention, attention_head, decode_paged, gather_paged, visible_mask
 from .online import online_softmax, tiled_attention_head, merge_states
+from .backward import attention_backward, attention_backward_head
 
 __all__ = [
     "attention",
@@ -32,4 +34,6 @@ __all__ = [
     "online_softmax",
     "tiled_attention_head",
     "merge_states",
+    "attention_backward",
+    "attention_backward_head",
 ]
