@@ -9,6 +9,8 @@ computation runs in the library's HIP kernels; there is no fallback.
     attn_fwd_f32(q, k, v, causal=False, window=0, scale=None)    fp32 prefill
     attn_decode_paged(q, kcache, vcache, block_table, seq_lens, ...)
     attn_decode_paged_workspace_size(B, Hq, d, block_size, max_blocks_per_seq)
+    attn_bwd(q, k, v, out, dout, lse, causal=False, window=0, scale=None)
+    attn_bwd_workspace_size(B, Hq, Nq)
     attn_status_str(code)
 
 Layouts: q [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d]; out like q; lse [B, Hq, Nq]
@@ -29,6 +31,8 @@ __all__ = [
     "attn_fwd_f32",
     "attn_decode_paged",
     "attn_decode_paged_workspace_size",
+    "attn_bwd",
+    "attn_bwd_workspace_size",
     "attn_status_str",
     "AttnError",
 ]
@@ -164,3 +168,49 @@ def attn_decode_paged(q, kcache, vcache, block_table, seq_lens, scale=None, wind
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "attn_decode_paged")
     return out, lse
+
+
+def attn_bwd_workspace_size(B: int, Hq: int, Nq: int) -> int:
+    return int(_lib.lib().attn_bwd_workspace_size(B, Hq, Nq))
+
+
+def attn_bwd(q, k, v, out, dout, lse, causal: bool = False, window: int = 0, scale=None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """bf16 backward of attn_fwd.  Returns (dq, dk, dv)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _dev(t, name, torch.bfloat16)
+    _dev(lse, "lse", torch.float32)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Nq,Hq,d], k and v [B,Nk,Hkv,d]")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have q's shape")
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk_ = k.shape
+    if Bk != B or dk_ != d:
+        raise ValueError("q and k disagree on batch or head dimension")
+    if lse.shape != (B, Hq, Nq):
+        raise ValueError("lse must be [B, Hq, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for t, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if t is None:
+            t = torch.empty_like(like)
+        else:
+            _dev(t, name, torch.bfloat16)
+            if t.shape != like.shape:
+                raise ValueError(f"{name} has the wrong shape")
+        outs.append(t)
+    dq, dk, dv = outs
+    need = attn_bwd_workspace_size(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device.type != "cuda":
+        raise ValueError("workspace must be on the GPU")
+    code = _lib.lib().attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+        B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), int(window), float(scale),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(code, "attn_bwd")
+    return dq, dk, dv

@@ -118,6 +118,30 @@ int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+size_t attn_bwd_workspace_size(int B, int Hq, int Nq) {
+  if (B < 0 || Hq < 1 || Nq < 0) return 0;
+  return attn::bwd_workspace_bytes(B, Hq, Nq);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+             int Nk, int d, int causal, int window, float scale, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  const int st = check_fwd(q, k, v, dq, B, Hq, Hkv, Nq, Nk, d, causal, window, 0);
+  if (st != ATTN_OK) return st;
+  if ((long long)B * Nq > 0 && (!out || !dout || !lse)) return ATTN_E_NULL;
+  if ((long long)B * Nk > 0 && (!dk || !dv)) return ATTN_E_NULL;
+  if (B > 65535 || Hq > 65535 || Hkv > 65535) return ATTN_E_SHAPE;  // grid y, z limits
+  if ((long long)B * Nq * Hq * d > (1LL << 40)) return ATTN_E_SHAPE;
+  if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
+  const size_t need = attn::bwd_workspace_bytes(B, Hq, Nq);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_E_WORKSPACE;
+  attn::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d,
+                  causal, window > 0 ? window : 0, scale, workspace};
+  const hipError_t e = attn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
 const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

@@ -1,0 +1,531 @@
+// Backward pass of exact softmax attention for bf16 Q/K/V on gfx950.
+//
+// Method: the backward pass recomputes the local probabilities from the
+// statistics the forward saved instead of storing the attention matrix
+// ("Ch. 3: MHA Limitations, MQA, GQA, and FlashAttention", section 3.5; the
+// float32 log-sum-exp of "Attention Is O(n^2): FlashAttention vs Linear
+// Attention", section "FlashAttention - Same FLOPs, Linear Memory").  With
+// P = exp(scale * Q K^T - LSE) over the visible keys, the gradients of
+// L = sum(dO * O) are
+//     dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
+//     dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q,
+// and a KV head shared by G query heads sums their dK and dV.
+//
+// Three kernels, no atomics (the results do not depend on scheduling):
+//   bwd_prep   D = rowsum(dO * O) and LSE * log2(e) per (b, h, row), into the
+//              workspace (a row with LSE = -inf, which sees no key, gets
+//              +inf, so that all its probabilities come out 0).
+//   bwd_dkdv   one work group per (128-key tile, KV head, batch); wave w owns
+//              32 keys, holding them as the B operand of
+//              v_mfma_f32_32x32x16_bf16 (lane l: key l % 32).  It walks the G
+//              query heads and their 32-row query blocks that see the tile:
+//                S  = Q K^T     A = Q rows from LDS, B = K (registers)
+//                dP = dO V^T    A = dO rows from LDS, B = V (registers)
+//              (lane l: key l % 32, 16 query rows), then P, dS, and
+//                dV^T += dO^T P   A = dO^T from the LDS transposing load
+//                dK^T += Q^T dS   A = Q^T likewise
+//              with P and dS converted to bf16 (round to nearest even) as the
+//              B operands straight from the score registers: the MFMA k index
+//              runs over the query rows in the same permuted order on both
+//              operands.
+//   bwd_dq     one work group per 128-row query tile of one head; wave w owns
+//              32 rows, holding Q and dO as B operands (lane l: row l % 32):
+//                S^T = K Q^T,  dP^T = V dO^T   A = K, V rows from LDS
+//                dQ^T += K^T dS^T              A = K^T from the transposing load
+//              so P, D and the log-sum-exp are one value per lane.
+// Tiles go through registers into LDS (double-buffered: the next tile's
+// global loads are in flight while the current one is computed).  Rows are
+// padded to a pitch of 2D + 16 bytes, which keeps both the row reads and the
+// transposing reads of the same tile free of most bank conflicts.
+#include "device_common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = kBwdWaves * 64;
+constexpr int kBlk = 32;  // MFMA block: 32 keys x 32 query rows
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dsum;   // [B, Hq, Nq]: D = rowsum(dO * O)
+  float* lse2;   // [B, Hq, Nq]: LSE * log2(e), +inf for a row without keys
+  int B, Hq, Hkv, group, Nq, Nk, causal, window;
+  float scale, sl2;
+};
+
+template <int D>
+struct BT {
+  static constexpr int KC = D / 16;            // k-chunks over the head dimension
+  static constexpr int NDB = D / 32;           // 32-feature blocks of dK^T, dV^T, dQ^T
+  static constexpr int PITCH = 2 * D + 16;     // LDS bytes per staged row
+  static constexpr int ROWB = 2 * D;           // global bytes per row
+  static constexpr int PIECES = ROWB / 16;     // 16-byte pieces per row
+};
+
+// ---------------------------------------------------------------------------
+// Shared tile helpers.
+
+// Stage `rows` rows (16-byte pieces) of a [N, H, D] tensor starting at row r0
+// into registers: piece p of the block = row p / PIECES, piece p % PIECES.
+// Rows at or past n_rows read as zero.
+template <int D, int ROWS>
+struct Stage {
+  static constexpr int NP = ROWS * BT<D>::PIECES / kBwdThreads;  // pieces per thread
+  static_assert(NP * kBwdThreads == ROWS * BT<D>::PIECES, "whole pieces per thread");
+  u32x4 r[NP];
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t row_stride, int r0, int n_rows,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + i * kBwdThreads;
+      const int row = p / BT<D>::PIECES, pc = p % BT<D>::PIECES;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r0 + row < n_rows)
+        x = *reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + row) * row_stride + pc * 8);
+      r[i] = x;
+    }
+  }
+  __device__ __forceinline__ void store(lds_u8* lds, uint32_t off, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + i * kBwdThreads;
+      const int row = p / BT<D>::PIECES, pc = p % BT<D>::PIECES;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + off + row * BT<D>::PITCH + pc * 16) = r[i];
+    }
+  }
+};
+
+// A operand (rows x k) of a 32x32x16 MFMA from a staged tile: lane l reads row
+// row0 + l % 32, features 16c + 8 (l / 32) .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const lds_u8* lds, uint32_t off, int lane, int c) {
+  const uint32_t a = off + (lane & 31) * BT<D>::PITCH + (16 * c + 8 * (lane >> 5)) * 2;
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
+}
+
+// A operand (features x rows) = the tile transposed, for feature block db and
+// row chunk kc (16 rows): the transposing load hands lane 4r+c of each 16-lane
+// group the 4 rows of source lanes r, r+4, r+8, r+12 at feature 4r+c, so lane
+// l gets feature 32 db + l % 32 and rows {4g..4g+3, 8+4g..8+4g+3} + 16 kc,
+// g = l / 32: the order in which the 32x32 accumulator layout holds rows.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* lds, uint32_t off, int lane, int db, int kc) {
+  const int G16 = lane >> 4, s16 = lane & 15;
+  const int row = kc * 16 + (G16 >> 1) * 4 + (s16 >> 2);
+  const int feat = db * 32 + 16 * (G16 & 1) + 4 * (s16 & 3);
+  const uint32_t a = off + row * BT<D>::PITCH + feat * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a + 8 * BT<D>::PITCH));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Row (or column) r of the 32x32 accumulator held in register r of lane l:
+// 4 (l / 32) + r % 4 + 8 (r / 4).
+__device__ __forceinline__ int acc_row(int lane, int r) { return 4 * (lane >> 5) + (r & 3) + 8 * (r >> 2); }
+
+__device__ __forceinline__ bool visible(int i, int j, int delta, int causal, int window) {
+  const int pos = i + delta;
+  if (causal && j > pos) return false;
+  if (window > 0 && pos - j >= window) return false;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// D and LSE * log2(e) per row.
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8;          // lanes per row (16 bytes each)
+  constexpr int RPB = 256 / LPR;      // rows per block step
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;
+  const int64_t rows = (int64_t)p.B * p.Nq * p.Hq;  // rows in [B, Nq, Hq] order
+  for (int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR; r < rows; r += (int64_t)gridDim.x * RPB) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p.dout + r * D + sub * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(p.o + r * D + sub * 8);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s += bf16lo_to_f32(a[i]) * bf16lo_to_f32(b[i]) + bf16hi_to_f32(a[i]) * bf16hi_to_f32(b[i]);
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, LPR);
+    if (sub == 0) {
+      const int h = (int)(r % p.Hq);
+      const int64_t bi = r / p.Hq;
+      const int i = (int)(bi % p.Nq);
+      const int b = (int)(bi / p.Nq);
+      const int64_t o = ((int64_t)b * p.Hq + h) * p.Nq + i;
+      const float l = p.lse[o];
+      p.dsum[o] = s;
+      p.lse2[o] = l == kNegInf ? __builtin_inff() : l * kLog2e;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p) {
+  using T = BT<D>;
+  constexpr int QTILE = T::PITCH * kBlk;  // bytes of one staged 32-row tile
+  // [buffer][Q, dO] tiles, then [buffer][lse2, D] (32 floats each)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * QTILE + 2 * 2 * kBlk * 4];
+  lds_u8* const lds = (lds_u8*)smem;
+  const uint32_t stat0 = 4 * QTILE;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int k0 = kt * kBwdWaves * kBlk;          // first key of the tile
+  const int kw0 = k0 + wave * kBlk;              // first key of this wave
+  const int key = kw0 + (lane & 31);             // this lane's key (column)
+  const int g = lane >> 5;
+  const int delta = p.Nk - p.Nq;
+  const int64_t kv_row = (int64_t)p.Hkv * D;
+  const int64_t q_row = (int64_t)p.Hq * D;
+
+  // K and V of the lane's key as B operands (features 16c + 8g .. +7)
+  bf16x8 kb[T::KC], vb[T::KC];
+  {
+    const int64_t off = ((int64_t)b * p.Nk + key) * kv_row + (int64_t)hk * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < T::KC; ++c) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (key < p.Nk) {
+        x = *reinterpret_cast<const u32x4*>(p.k + off + 16 * c);
+        y = *reinterpret_cast<const u32x4*>(p.v + off + 16 * c);
+      }
+      kb[c] = __builtin_bit_cast(bf16x8, x);
+      vb[c] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  f32x16 dkt[T::NDB], dvt[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) dkt[db] = dvt[db] = f32x16{};
+
+  // query rows that see some key of the tile: [qlo, qhi)
+  const int klast = min(p.Nk, k0 + kBwdWaves * kBlk) - 1;
+  int qlo = 0, qhi = p.Nq;
+  if (p.causal) qlo = max(0, k0 - delta);
+  if (p.window > 0) qhi = min(p.Nq, klast - delta + p.window);
+  const int nblk = qhi > qlo ? (qhi - (qlo & ~(kBlk - 1)) + kBlk - 1) / kBlk : 0;
+  const int q_first = qlo & ~(kBlk - 1);
+  const int steps = nblk * p.group;  // (head, block) pairs, head-major
+
+  Stage<D, kBlk> sq, sdo;
+  float st_l2 = 0.f, st_d = 0.f;  // lse2 and D of row tid (tid < 32)
+  auto fetch = [&](int s) {
+    const int h = hk * p.group + s / nblk;
+    const int i0 = q_first + (s % nblk) * kBlk;
+    const uint16_t* qb = p.q + (int64_t)b * p.Nq * q_row + (int64_t)h * D;
+    const uint16_t* ob = p.dout + (int64_t)b * p.Nq * q_row + (int64_t)h * D;
+    sq.load(qb, q_row, i0, p.Nq, tid);
+    sdo.load(ob, q_row, i0, p.Nq, tid);
+    if (tid < kBlk) {
+      const int i = i0 + tid;
+      const int64_t o = ((int64_t)b * p.Hq + h) * p.Nq + i;
+      st_l2 = i < p.Nq ? p.lse2[o] : __builtin_inff();
+      st_d = i < p.Nq ? p.dsum[o] : 0.f;
+    }
+  };
+  auto stash = [&](int buf) {
+    sq.store(lds, (2 * buf) * QTILE, tid);
+    sdo.store(lds, (2 * buf + 1) * QTILE, tid);
+    if (tid < kBlk) {
+      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + stat0 + (2 * buf) * kBlk * 4 + tid * 4) = st_l2;
+      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + stat0 + (2 * buf + 1) * kBlk * 4 + tid * 4) = st_d;
+    }
+  };
+
+  if (steps > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) fetch(s + 1);  // global loads in flight during the compute
+    const int i0 = q_first + (s % nblk) * kBlk;
+    const uint32_t qoff = (2 * buf) * QTILE, ooff = (2 * buf + 1) * QTILE;
+    const uint32_t loff = stat0 + (2 * buf) * kBlk * 4, doff = stat0 + (2 * buf + 1) * kBlk * 4;
+    // does this wave's 32 x 32 block hold any visible pair, and does it need a mask?
+    bool any = kw0 < p.Nk;
+    if (p.causal && kw0 > i0 + kBlk - 1 + delta) any = false;
+    if (p.window > 0 && i0 + delta - (kw0 + kBlk - 1) >= p.window) any = false;
+    const bool full = (!p.causal || kw0 + kBlk - 1 <= i0 + delta) &&
+                      (p.window <= 0 || i0 + kBlk - 1 + delta - kw0 < p.window);
+    if (any) {
+      // S = Q K^T and dP = dO V^T (lane: key, 16 rows)
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < T::KC; ++c) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, qoff, lane, c), kb[c], sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, ooff, lane, c), vb[c], dpacc, 0, 0, 0);
+      }
+      float pr[16], ds[16];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // rows 4g + 8t .. +3 of the block: their lse2 and D
+        const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + loff + (4 * g + 8 * t) * 4);
+        const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + doff + (4 * g + 8 * t) * 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * t + u;
+          float e = fast_exp2(sacc[r] * p.sl2 - l4[u]);
+          if (!full && !visible(i0 + acc_row(lane, r), key, delta, p.causal, p.window)) e = 0.f;
+          pr[r] = e;
+          ds[r] = e * (dpacc[r] - d4[u]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-row chunks
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        u32x4 pp, pd;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pp[i] = pack_bf16x2(pr[8 * kc + 2 * i], pr[8 * kc + 2 * i + 1]);
+          pd[i] = pack_bf16x2(ds[8 * kc + 2 * i], ds[8 * kc + 2 * i + 1]);
+        }
+        const bf16x8 bp = __builtin_bit_cast(bf16x8, pp), bd = __builtin_bit_cast(bf16x8, pd);
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) {
+          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, ooff, lane, db, kc), bp, dvt[db], 0, 0, 0);
+          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, qoff, lane, db, kc), bd, dkt[db], 0, 0, 0);
+        }
+      }
+    }
+    // the other buffer's readers (block s - 1) passed the previous barrier
+    if (s + 1 < steps) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds key `key`, features
+  // 32 db + 8 t + 4 g .. +3 in registers 4 t .. 4 t + 3.
+  if (key < p.Nk) {
+    const int64_t off = ((int64_t)b * p.Nk + key) * kv_row + (int64_t)hk * D;
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int f = 32 * db + 8 * t + 4 * g;
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(dkt[db][4 * t] * p.scale, dkt[db][4 * t + 1] * p.scale);
+        wk[1] = pack_bf16x2(dkt[db][4 * t + 2] * p.scale, dkt[db][4 * t + 3] * p.scale);
+        wv[0] = pack_bf16x2(dvt[db][4 * t], dvt[db][4 * t + 1]);
+        wv[1] = pack_bf16x2(dvt[db][4 * t + 2], dvt[db][4 * t + 3]);
+        *reinterpret_cast<u32x2*>(p.dk + off + f) = wk;
+        *reinterpret_cast<u32x2*>(p.dv + off + f) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) {
+  using T = BT<D>;
+  constexpr int KN = 64;                  // keys per step (two 32-key blocks)
+  constexpr int KTILE = T::PITCH * KN;    // bytes of one staged K or V tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * KTILE];
+  lds_u8* const lds = (lds_u8*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / p.group;
+  const int q0 = qt * kBwdWaves * kBlk;
+  const int qw0 = q0 + wave * kBlk;
+  const int row = qw0 + (lane & 31);       // this lane's query row (column of S^T)
+  const int g = lane >> 5;
+  const int delta = p.Nk - p.Nq;
+  const int64_t kv_row = (int64_t)p.Hkv * D;
+  const int64_t q_row = (int64_t)p.Hq * D;
+
+  bf16x8 qb[T::KC], ob[T::KC];
+  float l2 = __builtin_inff(), dd = 0.f;
+  {
+    const int64_t off = ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < T::KC; ++c) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (row < p.Nq) {
+        x = *reinterpret_cast<const u32x4*>(p.q + off + 16 * c);
+        y = *reinterpret_cast<const u32x4*>(p.dout + off + 16 * c);
+      }
+      qb[c] = __builtin_bit_cast(bf16x8, x);
+      ob[c] = __builtin_bit_cast(bf16x8, y);
+    }
+    if (row < p.Nq) {
+      const int64_t o = ((int64_t)b * p.Hq + h) * p.Nq + row;
+      l2 = p.lse2[o];
+      dd = p.dsum[o];
+    }
+  }
+  f32x16 dqt[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) dqt[db] = f32x16{};
+
+  // keys some row of the tile sees: [jlo, jhi)
+  const int qlast = min(p.Nq, q0 + kBwdWaves * kBlk) - 1;
+  int jlo = 0, jhi = p.Nk;
+  if (p.causal) jhi = min(p.Nk, qlast + delta + 1);
+  if (p.window > 0) jlo = max(0, q0 + delta - p.window + 1);
+  const int j_first = jlo & ~(KN - 1);
+  const int steps = jhi > j_first ? (jhi - j_first + KN - 1) / KN : 0;
+
+  Stage<D, KN> sk, sv;
+  const uint16_t* kbase = p.k + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
+  const uint16_t* vbase = p.v + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
+  auto fetch = [&](int s) {
+    sk.load(kbase, kv_row, j_first + s * KN, p.Nk, tid);
+    sv.load(vbase, kv_row, j_first + s * KN, p.Nk, tid);
+  };
+  auto stash = [&](int buf) {
+    sk.store(lds, (2 * buf) * KTILE, tid);
+    sv.store(lds, (2 * buf + 1) * KTILE, tid);
+  };
+  if (steps > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) fetch(s + 1);
+    const int j0 = j_first + s * KN;
+    const uint32_t koff = (2 * buf) * KTILE, voff = (2 * buf + 1) * KTILE;
+#pragma unroll
+    for (int kb2 = 0; kb2 < KN / kBlk; ++kb2) {
+      const int jb = j0 + kb2 * kBlk;  // first key of the 32-key block
+      bool any = qw0 < p.Nq && jb < p.Nk;
+      if (p.causal && jb > qw0 + kBlk - 1 + delta) any = false;
+      if (p.window > 0 && qw0 + delta - (jb + kBlk - 1) >= p.window) any = false;
+      const bool full = (!p.causal || jb + kBlk - 1 <= qw0 + delta) &&
+                        (p.window <= 0 || qw0 + kBlk - 1 + delta - jb < p.window);
+      if (!any) continue;
+      const uint32_t kb_off = koff + kb2 * kBlk * T::PITCH, vb_off = voff + kb2 * kBlk * T::PITCH;
+      // S^T = K Q^T, dP^T = V dO^T (lane: row, 16 keys)
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < T::KC; ++c) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, kb_off, lane, c), qb[c], sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, vb_off, lane, c), ob[c], dpacc, 0, 0, 0);
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = fast_exp2(sacc[r] * p.sl2 - l2);
+        if (!full && !visible(row, jb + acc_row(lane, r), delta, p.causal, p.window)) e = 0.f;
+        ds[r] = e * (dpacc[r] - dd);
+      }
+      // dQ^T += K^T dS^T over the block's two 16-key chunks
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        u32x4 pd;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pd[i] = pack_bf16x2(ds[8 * kc + 2 * i], ds[8 * kc + 2 * i + 1]);
+        const bf16x8 bd = __builtin_bit_cast(bf16x8, pd);
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db)
+          dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, kb_off, lane, db, kc), bd, dqt[db], 0, 0, 0);
+      }
+    }
+    // the other buffer's readers (block s - 1) passed the previous barrier
+    if (s + 1 < steps) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (row < p.Nq) {
+    const int64_t off = ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int f = 32 * db + 8 * t + 4 * g;
+        u32x2 w;
+        w[0] = pack_bf16x2(dqt[db][4 * t] * p.scale, dqt[db][4 * t + 1] * p.scale);
+        w[1] = pack_bf16x2(dqt[db][4 * t + 2] * p.scale, dqt[db][4 * t + 3] * p.scale);
+        *reinterpret_cast<u32x2*>(p.dq + off + f) = w;
+      }
+  }
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int Hq, int Nq) {
+  const size_t n = (size_t)B * Hq * Nq;
+  return 2 * ((n * sizeof(float) + 255) / 256 * 256);
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<const uint16_t*>(a.out);
+  p.dout = static_cast<const uint16_t*>(a.dout);
+  p.lse = a.lse;
+  p.dq = static_cast<uint16_t*>(a.dq);
+  p.dk = static_cast<uint16_t*>(a.dk);
+  p.dv = static_cast<uint16_t*>(a.dv);
+  const size_t n = (size_t)a.B * a.Hq * a.Nq;
+  char* ws = static_cast<char*>(a.workspace);
+  p.dsum = reinterpret_cast<float*>(ws);
+  p.lse2 = reinterpret_cast<float*>(ws + (n * sizeof(float) + 255) / 256 * 256);
+  p.B = a.B;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.group = a.Hq / a.Hkv;
+  p.Nq = a.Nq;
+  p.Nk = a.Nk;
+  p.causal = a.causal;
+  p.window = a.window;
+  p.scale = a.scale;
+  p.sl2 = a.scale * kLog2e;
+
+  const long long rows = (long long)a.B * a.Nq * a.Hq;
+  const int rpb = 256 / (a.d / 8);
+  const long long nb = (rows + rpb - 1) / rpb;
+  const dim3 g0((unsigned)(nb < 65536 ? nb : 65536));
+  const dim3 g1((a.Nk + kBwdWaves * kBlk - 1) / (kBwdWaves * kBlk), a.Hkv, a.B);
+  const dim3 g2((a.Nq + kBwdWaves * kBlk - 1) / (kBwdWaves * kBlk), a.Hq, a.B);
+  // an empty grid is not launched: with Nq = 0 the dK/dV kernel still writes
+  // zeros, with Nk = 0 the dQ kernel does
+  if (rows > 0) {
+    if (a.d == 128)
+      hipLaunchKernelGGL(bwd_prep_kernel<128>, g0, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(bwd_prep_kernel<64>, g0, dim3(256), 0, stream, p);
+  }
+  if ((long long)g1.x * g1.y * g1.z > 0) {
+    if (a.d == 128)
+      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, g1, dim3(kBwdThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, g1, dim3(kBwdThreads), 0, stream, p);
+  }
+  if ((long long)g2.x * g2.y * g2.z > 0) {
+    if (a.d == 128)
+      hipLaunchKernelGGL(bwd_dq_kernel<128>, g2, dim3(kBwdThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(bwd_dq_kernel<64>, g2, dim3(kBwdThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

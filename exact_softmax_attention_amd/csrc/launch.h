@@ -40,6 +40,25 @@ struct DecodeArgs {
   void* workspace;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Nq, Nk, d;
+  int causal, window;
+  float scale;
+  void* workspace;
+};
+
+size_t bwd_workspace_bytes(int B, int Hq, int Nq);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+
 size_t decode_workspace_bytes(int B, int Hq, int d, int block_size, int max_blocks_per_seq);
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
 

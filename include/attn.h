@@ -10,7 +10,9 @@
  *                            causal and sliding-window masks and grouped
  *                            K/V heads (MHA, GQA, MQA);
  *   attn_decode_paged        one query per sequence over a block-paged KV
- *                            cache, split along the keys with a final merge.
+ *                            cache, split along the keys with a final merge;
+ *   attn_bwd                 the gradients of attn_fwd (bf16), recomputing
+ *                            the probabilities from the saved log-sum-exp.
  *
  * Sources (pages; section names as printed):
  *   - "Attention Is O(n^2): FlashAttention vs Linear Attention", "Why
@@ -139,6 +141,42 @@ int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
                       int B, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
                       int num_blocks, int window, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs (two float32 values per query row
+ * and head; 0 for invalid sizes).  Pure host function; no HIP call.
+ */
+size_t attn_bwd_workspace_size(int B, int Hq, int Nq);
+
+/*
+ * Backward pass of attn_fwd: the gradients of L = sum(dout * out) with
+ * respect to q, k and v, recomputing the probabilities from the saved
+ * log-sum-exp instead of storing them ("Ch. 3: MHA Limitations, MQA, GQA,
+ * and FlashAttention", 3.5).  With P = exp(scale * q k^T - lse) over the
+ * visible keys:
+ *   dv = P^T dout,  dS = P * (dout v^T - D) with D_i = sum_c dout_ic out_ic,
+ *   dq = scale * dS k,  dk = scale * dS^T q,
+ * and a K/V head shared by several query heads receives the sum of their dk
+ * and dv.
+ *
+ *   q, out, dout  [B, Nq, Hq, d] bf16 (out and lse as attn_fwd returned them)
+ *   k, v          [B, Nk, Hkv, d] bf16
+ *   lse           [B, Hq, Nq] float32 (natural log; -inf for a row without keys)
+ *   dq            [B, Nq, Hq, d] bf16 (rounded to nearest even)
+ *   dk, dv        [B, Nk, Hkv, d] bf16
+ *   workspace     device scratch of at least attn_bwd_workspace_size(B, Hq, Nq)
+ *                 bytes, owned by the caller; its contents on entry do not matter
+ *
+ * Sizes, masks (causal, window, scale) and their rules are those of attn_fwd;
+ * B, Hq, Hkv <= 65535 (grid limits).  Every element of dq, dk and dv is
+ * written (zero where nothing contributes).  The result does not depend on
+ * scheduling: no atomics.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d,
+             int causal, int window, float scale,
+             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable text for a status code. */
 const char* attn_status_str(int status);

@@ -101,3 +101,30 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         _lib.lib()
+
+
+def _bwd(ptr=FAKE, lse=FAKE, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, causal=0, window=0,
+         ws=FAKE, ws_bytes=1 << 20):
+    return _lib.lib().attn_bwd(ptr, ptr, ptr, ptr, ptr, lse, ptr, ptr, ptr, B, Hq, Hkv, Nq, Nk,
+                               d, causal, window, 0.125, ws, ws_bytes, None)
+
+
+def test_bwd_workspace_size():
+    L = _lib.lib()
+    n = L.attn_bwd_workspace_size(2, 4, 1000)
+    assert n >= 2 * 2 * 4 * 1000 * 4 and n % 256 == 0
+    assert L.attn_bwd_workspace_size(-1, 4, 10) == 0
+    assert L.attn_bwd_workspace_size(1, 0, 10) == 0
+
+
+def test_bwd_validation():
+    assert _bwd(ptr=None) == _lib.ATTN_E_NULL
+    assert _bwd(lse=None) == _lib.ATTN_E_NULL
+    assert _bwd(Hq=3, Hkv=2) == _lib.ATTN_E_SHAPE
+    assert _bwd(d=96) == _lib.ATTN_E_HEADDIM
+    assert _bwd(window=4) == _lib.ATTN_E_MASK
+    assert _bwd(causal=1, Nq=9, Nk=8) == _lib.ATTN_E_SHAPE
+    assert _bwd(B=70000) == _lib.ATTN_E_SHAPE
+    assert _bwd(ws=None) == _lib.ATTN_E_WORKSPACE
+    assert _bwd(ws_bytes=16) == _lib.ATTN_E_WORKSPACE
+    assert _bwd(ptr=None, lse=None, B=0) == _lib.ATTN_OK

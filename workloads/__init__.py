@@ -38,6 +38,7 @@ __all__ = [
     "DENSE_CONFIGS",
     "PAGED_CONFIGS",
     "make_dense",
+    "make_dout",
     "make_paged",
     "draw_normal",
 ]
@@ -151,6 +152,11 @@ def make_dense(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int,
     k = _to(draw_normal(seed, 1, (B, Nk, Hkv, d)), dtype)
     v = _to(draw_normal(seed, 2, (B, Nk, Hkv, d)), dtype)
     return q, k, v
+
+
+def make_dout(B: int, Nq: int, Hq: int, d: int, seed: int, dtype: str = "bf16"):
+    """The upstream gradient dO [B, Nq, Hq, d] of a backward pass (tag 3 of ``seed``)."""
+    return _to(draw_normal(seed, 3, (B, Nq, Hq, d)), dtype)
 
 
 def make_dense_config(cfg: DenseConfig):
