@@ -37,6 +37,8 @@
 // global loads are in flight while the current one is computed).  Rows are
 // padded to a pitch of 2D + 16 bytes, which keeps both the row reads and the
 // transposing reads of the same tile free of most bank conflicts.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -50,6 +52,18 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * 64;
 constexpr int kBlk = 32;  // MFMA block: 32 keys x 32 query rows
+constexpr int kAhead = 3; // tiles whose global loads are in flight (in registers)
+
+// f(integral_constant<0>) .. f(integral_constant<N-1>) while f returns true;
+// the index is a compile-time constant, so register sets can be chosen by it.
+template <int I, int N, typename F>
+__device__ __forceinline__ bool unroll_while(F&& f) {
+  if constexpr (I < N) {
+    if (!f(std::integral_constant<int, I>{})) return false;
+    return unroll_while<I + 1, N>(f);
+  }
+  return true;
+}
 
 struct BwdParams {
   const uint16_t* q;
@@ -79,25 +93,38 @@ struct BT {
 // ---------------------------------------------------------------------------
 // Shared tile helpers.
 
-// Stage `rows` rows (16-byte pieces) of a [N, H, D] tensor starting at row r0
+// Stage ROWS rows (16-byte pieces) of a [N, H, D] tensor starting at row r0
 // into registers: piece p of the block = row p / PIECES, piece p % PIECES.
-// Rows at or past n_rows read as zero.
+// The loads are buffer loads whose range ends with row n_rows - 1, so rows at
+// or past n_rows read as zero; each thread's byte offsets within the block
+// are fixed (StageOff) and only the scalar base moves from step to step.
 template <int D, int ROWS>
-struct Stage {
+struct StageOff {
   static constexpr int NP = ROWS * BT<D>::PIECES / kBwdThreads;  // pieces per thread
   static_assert(NP * kBwdThreads == ROWS * BT<D>::PIECES, "whole pieces per thread");
-  u32x4 r[NP];
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t row_stride, int r0, int n_rows,
-                                       int tid) {
+  int off[NP];
+  __device__ __forceinline__ StageOff(int64_t row_stride, int tid) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int p = tid + i * kBwdThreads;
-      const int row = p / BT<D>::PIECES, pc = p % BT<D>::PIECES;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (r0 + row < n_rows)
-        x = *reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + row) * row_stride + pc * 8);
-      r[i] = x;
+      off[i] = (int)((p / BT<D>::PIECES) * row_stride * 2) + (p % BT<D>::PIECES) * 16;
     }
+  }
+};
+
+template <int D, int ROWS>
+struct Stage {
+  static constexpr int NP = StageOff<D, ROWS>::NP;
+  u32x4 r[NP];
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t row_stride, int r0, int n_rows,
+                                       const StageOff<D, ROWS>& so) {
+    const int real = min(ROWS, n_rows - r0);  // rows of the block that exist (>= 1)
+    const int bytes = (int)((real - 1) * row_stride * 2) + 2 * D;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base + (int64_t)r0 * row_stride), (short)0, bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, so.off[i], 0, 0));
   }
   __device__ __forceinline__ void store(lds_u8* lds, uint32_t off, int tid) const {
 #pragma unroll
@@ -131,17 +158,6 @@ __device__ __forceinline__ bf16x8 tr_frag(const lds_u8* lds, uint32_t off, int l
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a + 8 * BT<D>::PITCH));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Row (or column) r of the 32x32 accumulator held in register r of lane l:
-// 4 (l / 32) + r % 4 + 8 (r / 4).
-__device__ __forceinline__ int acc_row(int lane, int r) { return 4 * (lane >> 5) + (r & 3) + 8 * (r >> 2); }
-
-__device__ __forceinline__ bool visible(int i, int j, int delta, int causal, int window) {
-  const int pos = i + delta;
-  if (causal && j > pos) return false;
-  if (window > 0 && pos - j >= window) return false;
-  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -227,39 +243,50 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
   const int q_first = qlo & ~(kBlk - 1);
   const int steps = nblk * p.group;  // (head, block) pairs, head-major
 
-  Stage<D, kBlk> sq, sdo;
-  float st_l2 = 0.f, st_d = 0.f;  // lse2 and D of row tid (tid < 32)
-  auto fetch = [&](int s) {
+  // step t's tiles travel in register set t % kAhead: loaded kAhead steps
+  // before they are computed, stored to LDS buffer t % 2 one step before
+  struct Set {
+    Stage<D, kBlk> q, o;
+    float l2, d;  // lse2 and D of row tid (tid < 32)
+  };
+  Set sets[kAhead];
+  const StageOff<D, kBlk> so(q_row, tid);
+  auto fetch = [&](Set& st, int s) __attribute__((always_inline)) {
+    if (s >= steps) return;
     const int h = hk * p.group + s / nblk;
     const int i0 = q_first + (s % nblk) * kBlk;
     const uint16_t* qb = p.q + (int64_t)b * p.Nq * q_row + (int64_t)h * D;
     const uint16_t* ob = p.dout + (int64_t)b * p.Nq * q_row + (int64_t)h * D;
-    sq.load(qb, q_row, i0, p.Nq, tid);
-    sdo.load(ob, q_row, i0, p.Nq, tid);
+    st.q.load(qb, q_row, i0, p.Nq, so);
+    st.o.load(ob, q_row, i0, p.Nq, so);
     if (tid < kBlk) {
       const int i = i0 + tid;
       const int64_t o = ((int64_t)b * p.Hq + h) * p.Nq + i;
-      st_l2 = i < p.Nq ? p.lse2[o] : __builtin_inff();
-      st_d = i < p.Nq ? p.dsum[o] : 0.f;
+      st.l2 = i < p.Nq ? p.lse2[o] : __builtin_inff();
+      st.d = i < p.Nq ? p.dsum[o] : 0.f;
     }
   };
-  auto stash = [&](int buf) {
-    sq.store(lds, (2 * buf) * QTILE, tid);
-    sdo.store(lds, (2 * buf + 1) * QTILE, tid);
+  auto stash = [&](const Set& st, int buf) __attribute__((always_inline)) {
+    st.q.store(lds, (2 * buf) * QTILE, tid);
+    st.o.store(lds, (2 * buf + 1) * QTILE, tid);
     if (tid < kBlk) {
-      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + stat0 + (2 * buf) * kBlk * 4 + tid * 4) = st_l2;
-      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + stat0 + (2 * buf + 1) * kBlk * 4 + tid * 4) = st_d;
+      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + stat0 + (2 * buf) * kBlk * 4 + tid * 4) = st.l2;
+      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + stat0 + (2 * buf + 1) * kBlk * 4 + tid * 4) = st.d;
     }
   };
 
+  unroll_while<0, kAhead>([&](auto J) { fetch(sets[J], J); return true; });
   if (steps > 0) {
-    fetch(0);
-    stash(0);
+    stash(sets[0], 0);
+    fetch(sets[0], kAhead);
   }
   __syncthreads();
-  for (int s = 0; s < steps; ++s) {
+  for (int s0 = 0; s0 < steps; s0 += kAhead) {
+   const bool more = unroll_while<0, kAhead>([&](auto U) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    const int s = s0 + u;
+    if (s >= steps) return false;
     const int buf = s & 1;
-    if (s + 1 < steps) fetch(s + 1);  // global loads in flight during the compute
     const int i0 = q_first + (s % nblk) * kBlk;
     const uint32_t qoff = (2 * buf) * QTILE, ooff = (2 * buf + 1) * QTILE;
     const uint32_t loff = stat0 + (2 * buf) * kBlk * 4, doff = stat0 + (2 * buf + 1) * kBlk * 4;
@@ -284,14 +311,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
         const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + loff + (4 * g + 8 * t) * 4);
         const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + doff + (4 * g + 8 * t) * 4);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * t + u;
-          float e = fast_exp2(sacc[r] * p.sl2 - l4[u]);
-          if (!full && !visible(i0 + acc_row(lane, r), key, delta, p.causal, p.window)) e = 0.f;
-          pr[r] = e;
-          ds[r] = e * (dpacc[r] - d4[u]);
+        for (int u = 0; u < 4; ++u) pr[4 * t + u] = fast_exp2(sacc[4 * t + u] * p.sl2 - l4[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ds[4 * t + u] = dpacc[4 * t + u] - d4[u];
+      }
+      if (!full) {
+        // register r holds row i0 + 4g + c(r), c(r) = r % 4 + 8 (r / 4); with
+        // t = key - (i0 + 4g + delta): hidden by causality when t > c(r), by the
+        // window when t <= c(r) - window
+        const int tk = key - (i0 + 4 * g + delta);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = (r & 3) + 8 * (r >> 2);
+          bool hide = p.causal && tk > c;
+          if (p.window > 0 && tk <= c - p.window) hide = true;
+          if (hide) pr[r] = 0.f;
         }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] *= pr[r];
       // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-row chunks
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
@@ -309,9 +347,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
         }
       }
     }
-    // the other buffer's readers (block s - 1) passed the previous barrier
-    if (s + 1 < steps) stash(buf ^ 1);
+    // the other buffer's readers (step s - 1) passed the previous barrier
+    if (s + 1 < steps) {
+      stash(sets[(u + 1) % kAhead], buf ^ 1);
+      fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
+    }
     __syncthreads();
+    return true;
+   });
+   if (!more) break;
   }
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds key `key`, features
@@ -389,25 +433,36 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) 
   const int j_first = jlo & ~(KN - 1);
   const int steps = jhi > j_first ? (jhi - j_first + KN - 1) / KN : 0;
 
-  Stage<D, KN> sk, sv;
+  // as in the dK/dV kernel: step t's K and V tiles travel in register set
+  // t % kAhead and LDS buffer t % 2
+  struct Set {
+    Stage<D, KN> k, v;
+  };
+  Set sets[kAhead];
   const uint16_t* kbase = p.k + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
   const uint16_t* vbase = p.v + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
-  auto fetch = [&](int s) {
-    sk.load(kbase, kv_row, j_first + s * KN, p.Nk, tid);
-    sv.load(vbase, kv_row, j_first + s * KN, p.Nk, tid);
+  const StageOff<D, KN> so(kv_row, tid);
+  auto fetch = [&](Set& st, int s) __attribute__((always_inline)) {
+    if (s >= steps) return;
+    st.k.load(kbase, kv_row, j_first + s * KN, p.Nk, so);
+    st.v.load(vbase, kv_row, j_first + s * KN, p.Nk, so);
   };
-  auto stash = [&](int buf) {
-    sk.store(lds, (2 * buf) * KTILE, tid);
-    sv.store(lds, (2 * buf + 1) * KTILE, tid);
+  auto stash = [&](const Set& st, int buf) __attribute__((always_inline)) {
+    st.k.store(lds, (2 * buf) * KTILE, tid);
+    st.v.store(lds, (2 * buf + 1) * KTILE, tid);
   };
+  unroll_while<0, kAhead>([&](auto J) { fetch(sets[J], J); return true; });
   if (steps > 0) {
-    fetch(0);
-    stash(0);
+    stash(sets[0], 0);
+    fetch(sets[0], kAhead);
   }
   __syncthreads();
-  for (int s = 0; s < steps; ++s) {
+  for (int s0 = 0; s0 < steps; s0 += kAhead) {
+   const bool more = unroll_while<0, kAhead>([&](auto U) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    const int s = s0 + u;
+    if (s >= steps) return false;
     const int buf = s & 1;
-    if (s + 1 < steps) fetch(s + 1);
     const int j0 = j_first + s * KN;
     const uint32_t koff = (2 * buf) * KTILE, voff = (2 * buf + 1) * KTILE;
 #pragma unroll
@@ -427,13 +482,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) 
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, kb_off, lane, c), qb[c], sacc, 0, 0, 0);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, vb_off, lane, c), ob[c], dpacc, 0, 0, 0);
       }
-      float ds[16];
+      float pr[16], ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = fast_exp2(sacc[r] * p.sl2 - l2);
-        if (!full && !visible(row, jb + acc_row(lane, r), delta, p.causal, p.window)) e = 0.f;
-        ds[r] = e * (dpacc[r] - dd);
+      for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(sacc[r] * p.sl2 - l2);
+      if (!full) {
+        // register r holds key jb + 4g + c(r); with t = jb + 4g - (row + delta)
+        // the key is past the row's position when t + c(r) > 0 and before its
+        // window when t + c(r) <= -window
+        const int tk = jb + 4 * g - (row + delta);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = (r & 3) + 8 * (r >> 2);
+          bool hide = p.causal && tk + c > 0;
+          if (p.window > 0 && tk + c <= -p.window) hide = true;
+          if (hide) pr[r] = 0.f;
+        }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dpacc[r] - dd);
       // dQ^T += K^T dS^T over the block's two 16-key chunks
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
@@ -447,8 +513,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) 
       }
     }
     // the other buffer's readers (block s - 1) passed the previous barrier
-    if (s + 1 < steps) stash(buf ^ 1);
+    if (s + 1 < steps) {
+      stash(sets[(u + 1) % kAhead], buf ^ 1);
+      fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
+    }
     __syncthreads();
+    return true;
+   });
+   if (!more) break;
   }
 
   if (row < p.Nq) {
