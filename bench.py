@@ -24,6 +24,11 @@ four rocprofv3 --pmc runs under DIR (fetch/, write/ of this bench, and
 copy_fetch/, copy_write/ of `--mode copy`): each counter is scaled by what it
 reads for the plain 1 GiB device copy.
 
+The backward pass (attn_bwd, the gradients of the same prefill workload for a
+seeded dO) is timed after the steps, on its own, and reported under
+`backward` (TFLOP/s counting 2.5x the forward's flops, against the bf16 MFMA
+peak); it is not part of the step.  --skip-backward leaves it out.
+
 Other workloads can be timed with --workload NAME (one of the dense configs);
 the default line is the one described above.
 """
@@ -74,6 +79,7 @@ def parse():
     ap.add_argument("--workload", default=None,
                     help="time only this dense workload's forward (extra lines)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: a plain device copy of known size (counter calibration)")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
@@ -201,7 +207,8 @@ def main():
 
     import torch
     import workloads
-    from exact_softmax_attention_amd import attn_decode_paged, attn_fwd, metrics
+    from exact_softmax_attention_amd import (attn_bwd, attn_bwd_workspace_size,
+                                             attn_decode_paged, attn_fwd, metrics)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -304,6 +311,27 @@ def main():
                                       "kernels": "decode_split_kernel<128> + "
                                                  "decode_combine_kernel<128>",
                                       "algorithmic_bytes": nbytes}}
+    if not args.skip_backward:
+        print("bench: backward", file=sys.stderr, flush=True)
+        do = workloads.make_dout(cfg.B, cfg.Nq, cfg.Hq, cfg.d, cfg.seed).to(dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        bws = torch.empty(max(1, attn_bwd_workspace_size(cfg.B, cfg.Hq, cfg.Nq)),
+                          dtype=torch.uint8, device=dev)
+        fwd()
+
+        def bwd():
+            attn_bwd(qd, kd, vd, out, do, lse, causal=cfg.causal, window=cfg.window,
+                     scale=cfg.scale, dq=dq, dk=dk, dv=dv, workspace=bws)
+
+        bper, _ = time_loop([bwd], max(2, args.steps // 2), max(1, args.warmup), torch)
+        bflops = metrics.bwd_flops(cfg.B, cfg.Hq, cfg.Nq, cfg.Nk, cfg.d, cfg.causal, cfg.window)
+        btf = bflops / (bper[0] * 1e-3) / 1e12
+        res["backward"] = {"value": round(btf, 2), "unit": "TFLOP/s", "ms": round(bper[0], 4),
+                           "workload": name, "flop_per_call": bflops,
+                           "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel",
+                           "roofline": {"bound": "mfma", "achieved": round(btf, 2),
+                                        "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(btf / metrics.PEAK_BF16_TFLOPS, 4)}}
     if not args.skip_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(q, k, v, cfg)

@@ -41,6 +41,12 @@ def fwd_flops(B: int, Hq: int, Nq: int, Nk: int, d: int, causal: bool, window: i
     return 4.0 * d * visible_pairs(Nq, Nk, causal, window) * B * Hq
 
 
+def bwd_flops(B: int, Hq: int, Nq: int, Nk: int, d: int, causal: bool, window: int) -> float:
+    """Algorithmic flops of the backward pass: five products the size of the
+    forward's two (S recomputed, dP = dO V^T, dV, dK, dQ), i.e. 2.5x forward."""
+    return 2.5 * fwd_flops(B, Hq, Nq, Nk, d, causal, window)
+
+
 def fwd_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, elt: int = 2,
               with_lse: bool = True) -> int:
     qo = 2 * B * Nq * Hq * d * elt
