@@ -89,3 +89,39 @@ def test_deterministic():
     b = _run(q, k, v, do, True, 0, 0.0883883)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def _full(name, kv_heads):
+    """The bench's backward call on a full workload; every gradient of the
+    listed (batch, KV head) groups is checked: dQ of their query heads, dK and
+    dV summed over those heads."""
+    cfg = workloads.DENSE_CONFIGS[name]
+    print(f"config {name}: generating inputs", flush=True)
+    q, k, v = workloads.make_dense_config(cfg)
+    do = workloads.make_dout(cfg.B, cfg.Nq, cfg.Hq, cfg.d, cfg.seed)
+    dq, dk, dv = _run(q, k, v, do, cfg.causal, cfg.window, cfg.scale)
+    print(f"config {name}: kernels done", flush=True)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all().item()
+    G = cfg.Hq // cfg.Hkv
+    for b, hk in kv_heads:
+        rk_sum = rv_sum = 0.0
+        for h in range(hk * G, hk * G + G):
+            rq, rk, rv, _ = oracle.attention_backward_head(
+                q[b, :, h], k[b, :, hk], v[b, :, hk], do[b, :, h], cfg.scale, cfg.causal,
+                cfg.window)
+            check_grad(dq[b, :, h], rq, f"{name} b{b} h{h} dq")
+            rk_sum = rk_sum + rk
+            rv_sum = rv_sum + rv
+        check_grad(dk[b, :, hk], rk_sum, f"{name} b{b} hk{hk} dk")
+        check_grad(dv[b, :, hk], rv_sum, f"{name} b{b} hk{hk} dv")
+
+
+def test_mha_causal_8k_full_size():
+    _full("mha_causal_8k", [(0, 0), (3, 31)])
+
+
+def test_gqa_causal_16k_full_size():
+    _full("gqa_causal_16k", [(1, 7)])
