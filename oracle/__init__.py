@@ -17,6 +17,7 @@ Modules:
   online     - the online softmax and the tiled recurrence (pages' algorithm)
   brute      - pure-Python loops with math.fsum, for n <= 16
   backward   - fp64 gradients dQ, dK, dV of the plain definition
+  varlen     - the definition applied per sequence of a packed batch
 
 Every function is pinned by the ``-m "not gpu"`` tests in ``tests/`` against
 the pages' printed values, closed forms and invariants.
@@ -24,6 +25,7 @@ the pages' printed values, closed forms and invariants.
 from .attention import attention, attention_head, decode_paged, gather_paged, visible_mask
 from .online import online_softmax, tiled_attention_head, merge_states
 from .backward import attention_backward, attention_backward_head
+from .varlen import attention_varlen
 
 __all__ = [
     "attention",
@@ -36,4 +38,5 @@ __all__ = [
     "merge_states",
     "attention_backward",
     "attention_backward_head",
+    "attention_varlen",
 ]

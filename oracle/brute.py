@@ -54,3 +54,61 @@ def attention_brute(q, k, v, scale: float, causal: bool = False, window: int = 0
                     O[b][i][h][c] = math.fsum(w[j] * v[b][j][g][c] for j in keys) / total
                 LSE[b][h][i] = math.log(total)
     return O, LSE
+
+
+def attention_brute_packed(q, k, v, cu_q, cu_k, scale: float, causal: bool = False,
+                           window: int = 0):
+    """Packed sequences over one token axis, by brute force (tiny inputs).
+
+    q [total_q][Hq][d], k and v [total_k][Hkv][d] as nested lists; cu_q, cu_k
+    the boundary offsets (sequence s owns rows cu[s] .. cu[s+1]-1).  Every
+    packed query row is tested against every packed key row: the key is seen
+    when both belong to the same sequence and the key's index within it passes
+    the causal and window tests at the row's position within it (bottom-right:
+    row i of a sequence with nq queries and nk keys sits at i + nk - nq).
+
+    Returns (O [total_q][Hq][d], LSE [Hq][total_q]); a row outside every
+    sequence, or seeing no key, gives O = 0 and LSE = -inf.
+    """
+    total_q, Hq, d = len(q), len(q[0]) if q else 0, len(q[0][0]) if q else 0
+    total_k = len(k)
+    Hkv = len(k[0]) if k else 1
+    dv = len(v[0][0]) if v else d
+    group = Hq // Hkv if Hq else 1
+    S = len(cu_q) - 1
+
+    def owner(cu, t):
+        for s in range(S):
+            if cu[s] <= t < cu[s + 1]:
+                return s
+        return -1
+
+    O = [[[0.0] * dv for _ in range(Hq)] for _ in range(total_q)]
+    LSE = [[-math.inf] * total_q for _ in range(Hq)]
+    for i in range(total_q):
+        s = owner(cu_q, i)
+        if s < 0:
+            continue
+        nq, nk = cu_q[s + 1] - cu_q[s], cu_k[s + 1] - cu_k[s]
+        pos = (i - cu_q[s]) + (nk - nq)
+        keys = []
+        for j in range(total_k):
+            if owner(cu_k, j) != s:
+                continue
+            jj = j - cu_k[s]
+            if causal and jj > pos:
+                continue
+            if window > 0 and pos - jj >= window:
+                continue
+            keys.append(j)
+        if not keys:
+            continue
+        for h in range(Hq):
+            g = h // group
+            w = {j: math.exp(scale * math.fsum(q[i][h][c] * k[j][g][c] for c in range(d)))
+                 for j in keys}
+            total = math.fsum(w.values())
+            for c in range(dv):
+                O[i][h][c] = math.fsum(w[j] * v[j][g][c] for j in keys) / total
+            LSE[h][i] = math.log(total)
+    return O, LSE
