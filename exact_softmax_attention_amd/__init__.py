@@ -7,6 +7,7 @@ computation runs in the library's HIP kernels; there is no fallback.
 
     attn_fwd(q, k, v, causal=False, window=0, scale=None)        bf16 prefill
     attn_fwd_f32(q, k, v, causal=False, window=0, scale=None)    fp32 prefill
+    attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, ...)   bf16, packed sequences
     attn_decode_paged(q, kcache, vcache, block_table, seq_lens, ...)
     attn_decode_paged_workspace_size(B, Hq, d, block_size, max_blocks_per_seq)
     attn_bwd(q, k, v, out, dout, lse, causal=False, window=0, scale=None)
@@ -14,7 +15,8 @@ computation runs in the library's HIP kernels; there is no fallback.
     attn_status_str(code)
 
 Layouts: q [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d]; out like q; lse [B, Hq, Nq]
-float32.  Decode: q [B, Hq, d]; caches [num_blocks, block_size, Hkv, d];
+float32.  Packed sequences: q [total_q, Hq, d]; k, v [total_k, Hkv, d];
+cu_seqlens_q, cu_seqlens_k [num_seqs + 1] int32 on the GPU; lse [Hq, total_q].  Decode: q [B, Hq, d]; caches [num_blocks, block_size, Hkv, d];
 block_table [B, max_blocks] int32; seq_lens [B] int32; out [B, Hq, d];
 lse [B, Hq].
 """
@@ -29,6 +31,7 @@ from . import _lib
 __all__ = [
     "attn_fwd",
     "attn_fwd_f32",
+    "attn_fwd_varlen",
     "attn_decode_paged",
     "attn_decode_paged_workspace_size",
     "attn_bwd",
@@ -112,6 +115,51 @@ def attn_fwd(q, k, v, causal: bool = False, window: int = 0, scale=None, out=Non
              return_lse: bool = True):
     """bf16 attention forward.  Returns (out, lse); lse is None if not requested."""
     return _fwd("attn_fwd", torch.bfloat16, q, k, v, causal, window, scale, out, lse, return_lse)
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool = False, window: int = 0,
+                    scale=None, out=None, lse=None, return_lse: bool = True):
+    """bf16 forward over packed sequences.  Returns (out, lse); lse is None if not requested.
+
+    Sequence s owns rows cu_seqlens_q[s]:cu_seqlens_q[s+1] of q/out and rows
+    cu_seqlens_k[s]:cu_seqlens_k[s+1] of k/v, and attends only within itself.
+    """
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, name, torch.bfloat16)
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("expected q [total_q,Hq,d], k and v [total_k,Hkv,d]")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk = k.shape
+    if dk != d:
+        raise ValueError("q and k disagree on the head dimension")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape or \
+            cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be [num_seqs + 1]")
+    if not (q.device == k.device == v.device == cu_seqlens_q.device == cu_seqlens_k.device):
+        raise ValueError("all tensors must be on one device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if lse.shape != (Hq, total_q):
+            raise ValueError("lse must be [Hq, total_q]")
+    code = _lib.lib().attn_fwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, cu_seqlens_q.data_ptr(),
+        cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1, total_q, total_k, Hq, Hkv, d,
+        int(bool(causal)), int(window), float(scale), _stream(q.device))
+    _check(code, "attn_fwd_varlen")
+    return out, lse
 
 
 def attn_fwd_f32(q, k, v, causal: bool = False, window: int = 0, scale=None, out=None, lse=None,

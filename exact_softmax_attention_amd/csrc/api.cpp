@@ -86,6 +86,28 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* out, flo
                     true);
 }
 
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs, int total_q,
+                    int total_k, int Hq, int Hkv, int d, int causal, int window, float scale,
+                    void* stream) {
+  // the per-sequence lengths live on the device: the host checks the totals
+  if (num_seqs < 0 || total_q < 0 || total_k < 0) return ATTN_E_SHAPE;
+  const int st = check_common(num_seqs, Hq, Hkv, d);
+  if (st != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return ATTN_E_MASK;
+  if (window > 0 && !causal) return ATTN_E_MASK;
+  if (attn::fwd_bf16_varlen_grid(num_seqs, Hq, total_q) > INT_MAX) return ATTN_E_SHAPE;
+  if ((long long)Hkv * d > (1LL << 22)) return ATTN_E_SHAPE;
+  if (num_seqs == 0 || total_q == 0) return ATTN_OK;
+  if (!q || !out || !cu_seqlens_q || !cu_seqlens_k) return ATTN_E_NULL;
+  if (total_k > 0 && (!k || !v)) return ATTN_E_NULL;
+  attn::FwdVarlenArgs a{q,        k,       v,       out, lse, cu_seqlens_q, cu_seqlens_k,
+                        num_seqs, total_q, total_k, Hq,  Hkv, d,            causal,
+                        window > 0 ? window : 0,    scale};
+  const hipError_t e = attn::launch_fwd_bf16_varlen(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
 size_t attn_decode_paged_workspace_size(int B, int Hq, int d, int block_size,
                                         int max_blocks_per_seq) {
   if (B < 0 || Hq < 1 || (d != 64 && d != 128) || block_size != 16 || max_blocks_per_seq < 1)

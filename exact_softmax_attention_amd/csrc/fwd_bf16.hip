@@ -98,6 +98,11 @@ struct Params {
   int slot;     // this launch's slot of scheduling counters
   int pairing;  // work units are pairs of query tiles (see the schedule)
   float sl2;  // scale * log2(e): scores are kept in the base-2 domain
+  // packed sequences: boundaries of the query and key rows of each sequence,
+  // the total rows of each tensor, and the schedule's tile slots per head
+  const int* cu_q;
+  const int* cu_k;
+  int n_seqs, total_q, total_k, vtiles;
 };
 
 // Scheduling counters of the persistent kernel: slot s holds one item counter
@@ -162,6 +167,28 @@ __device__ __forceinline__ int floordiv(int a, int b) {  // b > 0
   return (a % b != 0 && a < 0) ? q - 1 : q;
 }
 
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+// Packed sequences: the sequence whose schedule slots hold slot v, i.e. the
+// largest s in [0, n) with start(s) = cu[s] / kBM + s <= v (start is strictly
+// increasing for nondecreasing cu; cu is clamped to [0, total] as read).  A
+// 64-way search: each round the wave's lanes test 64 evenly spaced
+// candidates and the count of passing lanes narrows the range 64-fold.  The
+// result stays in [0, n) whatever cu holds.
+__device__ __forceinline__ int find_seq(const int* cu, int n, int total, int v, int lane) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    bool pass = false;
+    if (idx < hi) pass = clampi(cu[idx], 0, total) / kBM + idx <= v;
+    const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(pass));
+    lo += (max(cnt, 1) - 1) * step;
+    hi = min(hi, lo + step);
+  }
+  return __builtin_amdgcn_readfirstlane(lo);
+}
+
 template <int I, int N, typename F>
 __device__ __forceinline__ bool unrolled_while(F&& f) {
   if constexpr (I < N) {
@@ -200,7 +227,7 @@ __device__ __forceinline__ bool unrolled_while(F&& f) {
 //
 // POS_SCALE: scale > 0, so the row maximum of scale*s is scale * max(s) and the
 // scaling folds into the exponent's FMA.  Otherwise every score is scaled first.
-template <int D, bool POS_SCALE>
+template <int D, bool POS_SCALE, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   using T = Tile<D>;
   constexpr int S = kSlots;
@@ -236,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   const int Gx = (G - xcd + kXcd - 1) / kXcd;
   const int nq = p.n_qtiles;
   const int per_head = p.pairing ? (nq + 1) / 2 : nq;
-  const int units = p.total / nq * per_head;
+  const int units = VARLEN ? p.total : p.total / nq * per_head;
   const int first = (int)((int64_t)units * groups_before / G);
   const int last = (int)((int64_t)units * (groups_before + Gx) / G);
   int* const ctr = g_sched + p.slot * (kXcd + 1);  // [xcd counters..., finished groups]
@@ -249,18 +276,56 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   // pairs: the middle (costliest under a window) first; tiles: heavy first
   const int j = per_head - 1 - (unit - bh * per_head);
   for (int e = 0; e < 2; ++e) {
-    if (e == 1 && (!p.pairing || j == nq - 1 - j)) break;
-    const int qt = p.pairing ? (e == 0 ? nq - 1 - j : j) : nq - 1 - (per_head - 1 - j);
+    if (e == 1 && (VARLEN || !p.pairing || j == nq - 1 - j)) break;
     if (e == 1) __syncthreads();  // the first tile's O staging is done with the ring
-    const int b = bh / p.Hq;
-    const int h = bh - b * p.Hq;
+    // this item: query tile qt of head h of sequence b, whose Nq query rows
+    // start at token row q_tok0 and Nk key rows at k_tok0
+    int b, h, qt, Nq, Nk;
+    int64_t q_tok0, k_tok0, lse0;
+    if constexpr (VARLEN) {
+      // unit = (KV head, tile slot, query head within the group); the slots
+      // of sequence s start at cu_q[s] / kBM + s, which leaves room for its
+      // tiles (heaviest first), and a slot past them is skipped
+      const int hg = unit % p.group;
+      const int rest = unit / p.group;
+      const int slot = rest % p.vtiles;
+      h = (rest / p.vtiles) * p.group + hg;
+      b = find_seq(p.cu_q, p.n_seqs, p.total_q, slot, lane);
+      const int q0 = clampi(p.cu_q[b], 0, p.total_q);
+      const int q1 = clampi(p.cu_q[b + 1], q0, p.total_q);
+      const int k0 = clampi(p.cu_k[b], 0, p.total_k);
+      const int k1 = clampi(p.cu_k[b + 1], k0, p.total_k);
+      Nq = q1 - q0;
+      Nk = k1 - k0;
+      const int off = slot - (q0 / kBM + b);
+      const int ntl = (Nq + kBM - 1) / kBM;
+      if (off < 0 || off >= ntl) {
+        // every wave has read s_unit before thread 0 writes the next unit
+        // (a real item passes several barriers in between)
+        __syncthreads();
+        break;
+      }
+      qt = ntl - 1 - off;
+      q_tok0 = q0;
+      k_tok0 = k0;
+      lse0 = (int64_t)h * p.total_q + q0;
+    } else {
+      qt = p.pairing ? (e == 0 ? nq - 1 - j : j) : nq - 1 - (per_head - 1 - j);
+      b = bh / p.Hq;
+      h = bh - b * p.Hq;
+      Nq = p.Nq;
+      Nk = p.Nk;
+      q_tok0 = (int64_t)b * Nq;
+      k_tok0 = (int64_t)b * Nk;
+      lse0 = ((int64_t)b * p.Hq + h) * Nq;
+    }
     const int hk = h / p.group;
     const int i0 = qt * kBM;
     const int qw0 = i0 + wave * kRowsPerWave;
-    const int delta = p.Nk - p.Nq;
+    const int delta = Nk - Nq;
 
-    int kv_end = p.Nk;
-    if (p.causal) kv_end = min(p.Nk, i0 + kBM + delta);
+    int kv_end = Nk;
+    if (p.causal) kv_end = min(Nk, i0 + kBM + delta);
     int kv_begin = 0;
     if (p.window > 0) kv_begin = max(0, i0 + delta - p.window + 1);
     const int t_begin = kv_begin / T::BN;
@@ -270,8 +335,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     const int64_t q_row = (int64_t)p.Hq * D;
     bf16x8 qf[T::KC];
     {
-      const int row = min(qw0 + n, p.Nq - 1);  // rows past the end compute garbage, never stored
-      const uint16_t* qp = p.q + ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D + g * 8;
+      const int row = min(qw0 + n, Nq - 1);  // rows past the end compute garbage, never stored
+      const uint16_t* qp = p.q + (q_tok0 + row) * q_row + (int64_t)h * D + g * 8;
   #pragma unroll
       for (int c = 0; c < T::KC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + c * 16);
     }
@@ -282,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     // fetches logical piece c ^ swizzle(r) of key row r.
     const int64_t kv_row = (int64_t)p.Hkv * D;                 // elements between keys
     const uint32_t kv_row_b = static_cast<uint32_t>(kv_row * 2);
-    const int64_t head_off = (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
+    const int64_t head_off = k_tok0 * kv_row + (int64_t)hk * D;
     const uint16_t* kbase = p.k + head_off;
     const uint16_t* vbase = p.v + head_off;
     int koff[T::LPW], voff[T::LPW];
@@ -301,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     const uint32_t tile_b = (uint32_t)T::BN * kv_row_b;  // bytes of a whole tile's rows
     uint32_t last_b = 0;  // bytes of the last visible tile: up to the end of key row Nk-1
     if (n_tiles > 0) {
-      const int rows = p.Nk - (t_begin + n_tiles - 1) * T::BN;  // >= 1
+      const int rows = Nk - (t_begin + n_tiles - 1) * T::BN;  // >= 1
       last_b = rows >= T::BN ? tile_b : (uint32_t)(rows - 1) * kv_row_b + T::ROWB;
     }
     const uint8_t* knext = reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t_begin * tile_b;
@@ -354,8 +419,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
 
     // Tiles [kf0, kf1) are visible to every row of this wave and need no mask.
     int kf0 = 0, kf1 = 0;
-    if (qw0 < p.Nq) {
-      int hi = min(n_tiles, p.Nk / T::BN - t_begin);  // before the key tail
+    if (qw0 < Nq) {
+      int hi = min(n_tiles, Nk / T::BN - t_begin);  // before the key tail
       if (p.causal) hi = min(hi, floordiv(qw0 + delta + 1, T::BN) - t_begin);
       int lo = 0;
       if (p.window > 0) lo = max(0, -floordiv(p.window - qw0 - kRowsPerWave - delta, T::BN) - t_begin);
@@ -364,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     }
     auto wave_skips = [&](int k) __attribute__((always_inline)) {
       const int j0 = (t_begin + k) * T::BN;
-      bool skip = qw0 >= p.Nq;
+      bool skip = qw0 >= Nq;
       if (p.causal && j0 > qw0 + kRowsPerWave - 1 + delta) skip = true;
       if (p.window > 0 && j0 + T::BN - 1 < qw0 + delta - p.window + 1) skip = true;
       return skip;
@@ -537,8 +602,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
           const int j0 = (t_begin + k) * T::BN;
           const int pos = qw0 + n + delta;  // this lane's row position
           const int base = j0 + 4 * g;      // key of offset 0 in this lane
-          if ((j0 + T::BN > p.Nk) || (p.causal && j0 + T::BN - 1 > qw0 + delta)) {
-            int hi = p.Nk - 1 - base;
+          if ((j0 + T::BN > Nk) || (p.causal && j0 + T::BN - 1 > qw0 + delta)) {
+            int hi = Nk - 1 - base;
             if (p.causal) hi = min(hi, pos - base);
             mask_above(hi);
           }
@@ -656,13 +721,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
         const int r = i * RPI + rr;
         const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
             lds + ostage + r * OPITCH + 16 * cc);
-        if (qw0 + r < p.Nq)
-          *reinterpret_cast<u32x4*>(p.o + ((int64_t)b * p.Nq + qw0 + r) * q_row + (int64_t)h * D + 8 * cc) = w;
+        if (qw0 + r < Nq)
+          *reinterpret_cast<u32x4*>(p.o + (q_tok0 + qw0 + r) * q_row + (int64_t)h * D + 8 * cc) = w;
       }
     }
     const int row = qw0 + n;
-    if (row < p.Nq && p.lse != nullptr && g == 0)
-      p.lse[((int64_t)b * p.Hq + h) * p.Nq + row] =
+    if (row < Nq && p.lse != nullptr && g == 0)
+      p.lse[lse0 + row] =
           l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
   // the O staging is done with the ring before the next unit's loads
@@ -687,8 +752,35 @@ long long fwd_bf16_grid(int B, int Hq, int Nq) {
   return (long long)B * Hq * ((Nq + kBM - 1) / kBM);
 }
 
+namespace {
+
+// one persistent work group per CU (the LDS ring admits one per CU); launches
+// take scheduling-counter slots in turn
+template <bool VARLEN>
+hipError_t launch(Params& p, int d, float scale, long long units, hipStream_t stream) {
+  static std::atomic<unsigned> launches{0};
+  p.slot = (int)(launches.fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
+  const int cus = device_cus();
+  const dim3 grid(units < cus ? (int)units : cus), block(kThreads);
+  const bool pos = scale > 0.f;
+  if (d == 128) {
+    if (pos)
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, true, VARLEN>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, false, VARLEN>), grid, block, 0, stream, p);
+  } else {
+    if (pos)
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, true, VARLEN>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, false, VARLEN>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  Params p;
+  Params p{};
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
   p.v = static_cast<const uint16_t*>(a.v);
@@ -705,28 +797,40 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.total = (int)fwd_bf16_grid(a.B, a.Hq, a.Nq);
   p.sl2 = a.scale * kLog2e;
   if (p.total == 0) return hipSuccess;
-  // one persistent work group per CU (the LDS ring admits one per CU)
-  static std::atomic<unsigned> launches{0};
-  p.slot = (int)(launches.fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
   // pair query tiles when there are enough pairs to fill the CUs
-  const int cus = device_cus();
   const long long pairs = (long long)(p.total / p.n_qtiles) * ((p.n_qtiles + 1) / 2);
-  p.pairing = pairs >= cus ? 1 : 0;
-  const long long units = p.pairing ? pairs : p.total;
-  const dim3 grid(units < cus ? (int)units : cus), block(kThreads);
-  const bool pos = a.scale > 0.f;
-  if (a.d == 128) {
-    if (pos)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, p);
-  } else {
-    if (pos)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, p);
-  }
-  return hipGetLastError();
+  p.pairing = pairs >= device_cus() ? 1 : 0;
+  return launch<false>(p, a.d, a.scale, p.pairing ? pairs : p.total, stream);
+}
+
+long long fwd_bf16_varlen_grid(int n_seqs, int Hq, int total_q) {
+  return (long long)Hq * (total_q / kBM + n_seqs);
+}
+
+hipError_t launch_fwd_bf16_varlen(const FwdVarlenArgs& a, hipStream_t stream) {
+  Params p{};
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<uint16_t*>(a.out);
+  p.lse = a.lse;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.group = a.Hq / a.Hkv;
+  p.causal = a.causal;
+  p.window = a.window;
+  p.sl2 = a.scale * kLog2e;
+  p.cu_q = a.cu_seqlens_q;
+  p.cu_k = a.cu_seqlens_k;
+  p.n_seqs = a.n_seqs;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
+  p.vtiles = a.total_q / kBM + a.n_seqs;
+  p.n_qtiles = 1;
+  p.pairing = 0;
+  p.total = (int)fwd_bf16_varlen_grid(a.n_seqs, a.Hq, a.total_q);
+  if (a.n_seqs == 0 || a.total_q == 0) return hipSuccess;
+  return launch<true>(p, a.d, a.scale, p.total, stream);
 }
 
 }  // namespace attn

@@ -27,6 +27,26 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 long long fwd_bf16_grid(int B, int Hq, int Nq);
 long long fwd_f32_grid(int B, int Hq, int Nq);
 
+// Packed sequences: sequence s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1])
+// of q/out (total_q rows) and key rows [cu_seqlens_k[s], cu_seqlens_k[s+1]) of
+// k/v (total_k rows); the cu arrays are device memory of n_seqs + 1 ints.
+struct FwdVarlenArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const int* cu_seqlens_q;
+  const int* cu_seqlens_k;
+  int n_seqs, total_q, total_k, Hq, Hkv, d;
+  int causal, window;
+  float scale;
+};
+
+hipError_t launch_fwd_bf16_varlen(const FwdVarlenArgs& a, hipStream_t stream);
+// Work units of the packed launch (for the size check).
+long long fwd_bf16_varlen_grid(int n_seqs, int Hq, int total_q);
+
 struct DecodeArgs {
   const void* q;
   const void* kcache;

@@ -41,6 +41,12 @@ def fwd_flops(B: int, Hq: int, Nq: int, Nk: int, d: int, causal: bool, window: i
     return 4.0 * d * visible_pairs(Nq, Nk, causal, window) * B * Hq
 
 
+def varlen_fwd_flops(lens_q, lens_k, Hq: int, d: int, causal: bool, window: int) -> float:
+    """Forward flops of packed sequences: each sequence's own visible pairs."""
+    pairs = sum(visible_pairs(int(a), int(b), causal, window) for a, b in zip(lens_q, lens_k))
+    return 4.0 * d * pairs * Hq
+
+
 def bwd_flops(B: int, Hq: int, Nq: int, Nk: int, d: int, causal: bool, window: int) -> float:
     """Algorithmic flops of the backward pass: five products the size of the
     forward's two (S recomputed, dP = dO V^T, dV, dK, dQ), i.e. 2.5x forward."""

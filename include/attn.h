@@ -9,6 +9,9 @@
  *                            score matrix never reaches device memory, with
  *                            causal and sliding-window masks and grouped
  *                            K/V heads (MHA, GQA, MQA);
+ *   attn_fwd_varlen          the same forward over packed sequences of
+ *                            different lengths (no padding), each attending
+ *                            only within itself;
  *   attn_decode_paged        one query per sequence over a block-paged KV
  *                            cache, split along the keys with a final merge;
  *   attn_bwd                 the gradients of attn_fwd (bf16), recomputing
@@ -29,7 +32,9 @@
  *   - "Inference Engineering", 2.5 "Optimizing Attention" (PagedAttention:
  *     the cache is split into blocks reached through a lookup table).
  *   - "How to Reduce Attention Computation Cost in LLM Training",
- *     "FlashAttention Is Table Stakes" (fused call on (B, N, H, d) bf16).
+ *     "FlashAttention Is Table Stakes" (fused call on (B, N, H, d) bf16;
+ *     packed sequence boundaries need variable-length kernels), the
+ *     comparison table and FAQ (sequence packing).
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; nothing is
@@ -103,6 +108,39 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse,
                  int B, int Hq, int Hkv, int Nq, int Nk, int d,
                  int causal, int window, float scale, void* stream);
+
+/*
+ * Forward over packed sequences ("How to Reduce Attention Computation Cost in
+ * LLM Training": packed sequence boundaries need variable-length kernels,
+ * section "FlashAttention Is Table Stakes Now"; packing many short sequences
+ * instead of padding them, the comparison table and the FAQ).  bf16 in and
+ * out, float32 accumulation, the kernel of attn_fwd.
+ *
+ *   q, out        [total_q, Hq, d]   bf16: the sequences' query rows back to back
+ *   k, v          [total_k, Hkv, d]  bf16: their key rows back to back
+ *   cu_seqlens_q  [num_seqs + 1] int32, DEVICE memory: sequence s owns query
+ *                 rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1
+ *   cu_seqlens_k  [num_seqs + 1] int32, DEVICE memory: likewise for key rows
+ *   lse           [Hq, total_q] float32, or NULL to skip it
+ *
+ * Each sequence attends only to its own keys; causal alignment and the
+ * window apply within the sequence (its query row i sits at i + nk - nq).
+ * A sequence may have more queries than keys: under causal its first rows
+ * see no key and get O = 0, LSE = -inf.  Rows of q outside every sequence
+ * are not written.
+ *
+ * The cu arrays must be nondecreasing with entries in [0, total]; values
+ * outside are clamped into range as read (no access leaves the tensors) but
+ * the results are then unspecified.  The host never reads them.
+ *
+ * Sizes: num_seqs, total_q, total_k >= 0 (num_seqs == 0 or total_q == 0 is
+ * a no-op); Hq, Hkv, d, causal and window as for attn_fwd;
+ * Hq * (total_q / 256 + num_seqs) <= INT_MAX (ATTN_E_SHAPE).
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                    int total_q, int total_k, int Hq, int Hkv, int d,
+                    int causal, int window, float scale, void* stream);
 
 /*
  * Bytes of device workspace attn_decode_paged needs for these sizes

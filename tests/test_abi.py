@@ -128,3 +128,24 @@ def test_bwd_validation():
     assert _bwd(ws=None) == _lib.ATTN_E_WORKSPACE
     assert _bwd(ws_bytes=16) == _lib.ATTN_E_WORKSPACE
     assert _bwd(ptr=None, lse=None, B=0) == _lib.ATTN_OK
+
+
+def _varlen(ptr=1 << 20, cu=1 << 21, n=3, tq=100, tk=120, Hq=8, Hkv=2, d=128, causal=1, window=0):
+    return _lib.lib().attn_fwd_varlen(ptr, ptr, ptr, ptr, None, cu, cu, n, tq, tk, Hq, Hkv, d,
+                                      causal, window, 0.1, None)
+
+
+def test_varlen_validation():
+    # every rejection happens on the host, before any HIP call
+    assert _varlen(ptr=None) == _lib.ATTN_E_NULL
+    assert _varlen(cu=None) == _lib.ATTN_E_NULL
+    assert _varlen(n=-1) == _lib.ATTN_E_SHAPE
+    assert _varlen(tq=-1) == _lib.ATTN_E_SHAPE
+    assert _varlen(Hq=3, Hkv=2) == _lib.ATTN_E_SHAPE
+    assert _varlen(d=80) == _lib.ATTN_E_HEADDIM
+    assert _varlen(causal=0, window=5) == _lib.ATTN_E_MASK
+    assert _varlen(causal=2) == _lib.ATTN_E_MASK
+    assert _varlen(Hq=1 << 16, Hkv=1, n=1 << 15) == _lib.ATTN_E_SHAPE  # schedule size
+    # empty problems are no-ops whatever the pointers
+    assert _varlen(ptr=None, cu=None, n=0) == _lib.ATTN_OK
+    assert _varlen(ptr=None, cu=None, tq=0) == _lib.ATTN_OK

@@ -41,6 +41,11 @@ __all__ = [
     "make_dout",
     "make_paged",
     "draw_normal",
+    "PackedConfig",
+    "PACKED_CONFIGS",
+    "draw_lengths",
+    "make_packed",
+    "make_packed_config",
 ]
 
 
@@ -105,6 +110,36 @@ PAGED_CONFIGS = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class PackedConfig:
+    """Packed sequences: lengths drawn by ``draw_lengths`` until ``total``
+    tokens, each sequence's queries and keys of the same length."""
+    name: str
+    total: int
+    mean_len: int
+    max_len: int
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    window: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+# Packed training batch: sequences averaging about 600 tokens, none longer
+# than 2048 ("How to Reduce Attention Computation Cost in LLM Training",
+# section "What Most Teams Get Wrong": such sequences padded to 2048), with
+# the 32 heads of 128 of that page's fused-kernel example.
+PACKED_CONFIGS = {
+    "packed_causal_64k_mean600": PackedConfig("packed_causal_64k_mean600", 65536, 600, 2048,
+                                              32, 32, 128, True, 0, 6),
+}
+
+
 CHUNK_ROWS = 4096
 _THREADS = min(16, os.cpu_count() or 1)
 
@@ -161,6 +196,41 @@ def make_dout(B: int, Nq: int, Hq: int, d: int, seed: int, dtype: str = "bf16"):
 
 def make_dense_config(cfg: DenseConfig):
     return make_dense(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, cfg.seed, cfg.dtype)
+
+
+def draw_lengths(total: int, mean_len: int, max_len: int, seed: int) -> np.ndarray:
+    """Sequence lengths summing to ``total``: from ``default_rng(seed)``, each
+    length is 1 + floor(exponential(mean_len - 1)) clipped to ``max_len``,
+    drawn until the sum reaches ``total``; the last one is cut to fit."""
+    rng = np.random.default_rng(seed)
+    lens = []
+    left = int(total)
+    while left > 0:
+        n = min(int(max_len), 1 + int(rng.exponential(mean_len - 1)), left)
+        lens.append(n)
+        left -= n
+    return np.asarray(lens, dtype=np.int64)
+
+
+def make_packed(lens_q, lens_k, Hq: int, Hkv: int, d: int, seed: int, dtype: str = "bf16"):
+    """Packed Q [sum(lens_q), Hq, d], K and V [sum(lens_k), Hkv, d] (tags 0, 1, 2
+    of ``seed``, drawn as one tensor each) and the int32 boundaries
+    cu_seqlens_q, cu_seqlens_k ([num_seqs + 1], starting at 0), as CPU tensors."""
+    lq = np.asarray(lens_q, dtype=np.int64)
+    lk = np.asarray(lens_k, dtype=np.int64)
+    if lq.shape != lk.shape:
+        raise ValueError("lens_q and lens_k differ in count")
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = _to(draw_normal(seed, 0, (int(cu_q[-1]), Hq, d)), dtype)
+    k = _to(draw_normal(seed, 1, (int(cu_k[-1]), Hkv, d)), dtype)
+    v = _to(draw_normal(seed, 2, (int(cu_k[-1]), Hkv, d)), dtype)
+    return q, k, v, torch.from_numpy(cu_q), torch.from_numpy(cu_k)
+
+
+def make_packed_config(cfg: PackedConfig):
+    lens = draw_lengths(cfg.total, cfg.mean_len, cfg.max_len, cfg.seed)
+    return make_packed(lens, lens, cfg.Hq, cfg.Hkv, cfg.d, cfg.seed, "bf16")
 
 
 def make_paged(B: int, Hq: int, Hkv: int, d: int, block_size: int, num_blocks: int,
