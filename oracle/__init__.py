@@ -13,7 +13,8 @@ NumPy code on tiny inputs.
 
 Modules:
   attention  - naive fp64 attention with causal/window masks, GQA/MQA head
-               sharing, log-sum-exp, and the paged-cache decode oracle
+               sharing, log-sum-exp, and the paged-cache decode and
+               chunked-prefill oracles
   online     - the online softmax and the tiled recurrence (pages' algorithm)
   brute      - pure-Python loops with math.fsum, for n <= 16
   backward   - fp64 gradients dQ, dK, dV of the plain definition
@@ -22,7 +23,8 @@ Modules:
 Every function is pinned by the ``-m "not gpu"`` tests in ``tests/`` against
 the pages' printed values, closed forms and invariants.
 """
-from .attention import attention, attention_head, decode_paged, gather_paged, visible_mask
+from .attention import (attention, attention_head, decode_paged, gather_paged, prefill_paged,
+                        visible_mask)
 from .online import online_softmax, tiled_attention_head, merge_states
 from .backward import attention_backward, attention_backward_head
 from .varlen import attention_varlen
@@ -31,6 +33,7 @@ __all__ = [
     "attention",
     "attention_head",
     "decode_paged",
+    "prefill_paged",
     "gather_paged",
     "visible_mask",
     "online_softmax",

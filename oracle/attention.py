@@ -192,3 +192,47 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, scale, window: int = 
             O[b, h] = o[0]
             L[b, h] = l[0]
     return O, L
+
+
+def prefill_paged(q, kcache, vcache, block_table, seq_lens, cu_seqlens_q, scale,
+                  window: int = 0, seqs=None):
+    """Chunked prefill over a paged cache: several new tokens per sequence.
+
+    Sequence s has seq_lens[s] cached tokens, the last Nq_s of which are its
+    new tokens, whose queries are rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1
+    of q [total_q, Hq, d]; their K/V are already in the cache ("Ch. 3",
+    section 3.1: a new token's K/V are appended before it attends; the GQA
+    code of its section 3.3 notes that attention over a cache needs its own
+    causal handling, the plain causal flag covering only equal lengths).  Query row i of the chunk sits at position seq_len - Nq_s + i
+    and sees the cached tokens up to that position (the last ``window`` of
+    them when window > 0): bottom-right causal, as in ``attention_head``.
+
+    Returns (O [total_q, Hq, d], LSE [Hq, total_q]) in float64.  A sequence
+    whose table names a block outside the pool, or whose length is negative,
+    gets NaN; rows of sequences not in ``seqs`` stay NaN.
+    """
+    total_q, Hq, d = q.shape
+    Hkv = kcache.shape[2]
+    G = Hq // Hkv
+    table = np.asarray(block_table.numpy() if hasattr(block_table, "numpy") else block_table)
+    lens = np.asarray(seq_lens.numpy() if hasattr(seq_lens, "numpy") else seq_lens)
+    cu = np.asarray(cu_seqlens_q.numpy() if hasattr(cu_seqlens_q, "numpy") else cu_seqlens_q)
+    O = np.full((total_q, Hq, d), np.nan)
+    L = np.full((Hq, total_q), np.nan)
+    for s in (range(len(lens)) if seqs is None else seqs):
+        n = int(lens[s])
+        q0, q1 = int(cu[s]), int(cu[s + 1])
+        if n < 0 or n > table.shape[1] * kcache.shape[1]:
+            continue
+        kc = gather_paged(kcache, table[s], n)
+        vc = gather_paged(vcache, table[s], n)
+        if kc is None or vc is None:
+            continue  # bad block id: NaN
+        qs = _f64(q[q0:q1])
+        for h in range(Hq):
+            o, l = attention_head(qs[:, h, :], kc[:, h // G, :], vc[:, h // G, :], scale,
+                                  causal=True, window=window)
+            O[q0:q1, h] = o
+            L[h, q0:q1] = l
+    return O, L
+

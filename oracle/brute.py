@@ -112,3 +112,37 @@ def attention_brute_packed(q, k, v, cu_q, cu_k, scale: float, causal: bool = Fal
                 O[i][h][c] = math.fsum(w[j] * v[j][g][c] for j in keys) / total
             LSE[h][i] = math.log(total)
     return O, LSE
+
+
+def prefill_paged_brute(q, kcache, vcache, block_table, seq_lens, cu_q, scale: float,
+                        window: int = 0):
+    """Chunked prefill over a paged cache by brute force (tiny inputs).
+
+    q [total_q][Hq][d]; kcache, vcache [num_blocks][block_size][Hkv][d];
+    block_table [S][max_blocks]; seq_lens [S]; cu_q [S + 1], all nested lists.
+    Each sequence's cached tokens are copied out one by one through the table
+    (token t: block table[s][t // block_size], slot t % block_size), then the
+    dense brute force runs on that sequence with the chunk's queries as the
+    last rows (bottom-right causal).  Returns (O [total_q][Hq][d],
+    LSE [Hq][total_q]); every block id must be valid.
+    """
+    total_q = len(q)
+    Hq, d = len(q[0]), len(q[0][0])
+    bs = len(kcache[0])
+    O = [[[0.0] * d for _ in range(Hq)] for _ in range(total_q)]
+    LSE = [[-math.inf] * total_q for _ in range(Hq)]
+    for s in range(len(seq_lens)):
+        n = seq_lens[s]
+        kk = [kcache[block_table[s][t // bs]][t % bs] for t in range(n)]
+        vv = [vcache[block_table[s][t // bs]][t % bs] for t in range(n)]
+        rows = q[cu_q[s]:cu_q[s + 1]]
+        if not rows:
+            continue
+        if n == 0:
+            continue
+        o, l = attention_brute([rows], [kk], [vv], scale, causal=True, window=window)
+        for i in range(len(rows)):
+            for h in range(Hq):
+                O[cu_q[s] + i][h] = o[0][i][h]
+                LSE[h][cu_q[s] + i] = l[0][h][i]
+    return O, LSE
