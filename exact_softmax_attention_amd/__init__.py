@@ -10,6 +10,7 @@ computation runs in the library's HIP kernels; there is no fallback.
     attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, ...)   bf16, packed sequences
     attn_decode_paged(q, kcache, vcache, block_table, seq_lens, ...)
     attn_decode_paged_workspace_size(B, Hq, d, block_size, max_blocks_per_seq)
+    attn_prefill_paged(q, kcache, vcache, block_table, seq_lens, cu_seqlens_q, ...)
     attn_bwd(q, k, v, out, dout, lse, causal=False, window=0, scale=None)
     attn_bwd_workspace_size(B, Hq, Nq)
     attn_status_str(code)
@@ -34,6 +35,7 @@ __all__ = [
     "attn_fwd_varlen",
     "attn_decode_paged",
     "attn_decode_paged_workspace_size",
+    "attn_prefill_paged",
     "attn_bwd",
     "attn_bwd_workspace_size",
     "attn_status_str",
@@ -215,6 +217,52 @@ def attn_decode_paged(q, kcache, vcache, block_table, seq_lens, scale=None, wind
         B, Hq, Hkv, d, block_size, max_blocks, num_blocks, int(window), float(scale),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "attn_decode_paged")
+    return out, lse
+
+
+def attn_prefill_paged(q, kcache, vcache, block_table, seq_lens, cu_seqlens_q, scale=None,
+                       window: int = 0, out=None, lse=None, return_lse: bool = True):
+    """Chunked prefill over a paged cache (always causal).  Returns (out, lse).
+
+    Sequence s owns rows cu_seqlens_q[s]:cu_seqlens_q[s+1] of q/out: its new
+    tokens, the last of its seq_lens[s] cached tokens.
+    """
+    _dev(q, "q", torch.bfloat16)
+    _dev(kcache, "kcache", torch.bfloat16)
+    _dev(vcache, "vcache", torch.bfloat16)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    if q.dim() != 3 or kcache.dim() != 4 or vcache.shape != kcache.shape:
+        raise ValueError("expected q [total_q,Hq,d] and caches [num_blocks,block_size,Hkv,d]")
+    total_q, Hq, d = q.shape
+    num_blocks, block_size, Hkv, dk = kcache.shape
+    if dk != d:
+        raise ValueError("q and the cache disagree on the head dimension")
+    S = seq_lens.numel()
+    if block_table.dim() != 2 or block_table.shape[0] != S or seq_lens.dim() != 1 or \
+            cu_seqlens_q.shape != (S + 1,):
+        raise ValueError("block_table must be [S, max_blocks], seq_lens [S], cu_seqlens_q [S+1]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if lse.shape != (Hq, total_q):
+            raise ValueError("lse must be [Hq, total_q]")
+    code = _lib.lib().attn_prefill_paged(
+        q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), cu_seqlens_q.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, S, total_q, Hq, Hkv, d, block_size,
+        block_table.shape[1], num_blocks, int(window), float(scale), _stream(q.device))
+    _check(code, "attn_prefill_paged")
     return out, lse
 
 

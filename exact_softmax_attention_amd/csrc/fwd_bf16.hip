@@ -103,7 +103,17 @@ struct Params {
   const int* cu_q;
   const int* cu_k;
   int n_seqs, total_q, total_k, vtiles;
+  // paged cache: k and v are [num_blocks, 16, Hkv, D]; key t of sequence s is
+  // slot t % 16 of block table[s * max_blocks + t / 16]; seq_lens[s] keys
+  const int* table;
+  const int* seq_lens;
+  int max_blocks, num_blocks;
 };
+
+// What the kernel reads: dense [B, N, H, D] tensors, packed sequences
+// (cu_seqlens), or packed query chunks over a paged KV cache.
+enum Mode { kDense = 0, kVarlen = 1, kPaged = 2 };
+constexpr int kBlockTokens = 16;  // tokens per cache block
 
 // Scheduling counters of the persistent kernel: slot s holds one item counter
 // per XCD and a count of finished work groups.  Launches take slots in turn,
@@ -227,8 +237,10 @@ __device__ __forceinline__ bool unrolled_while(F&& f) {
 //
 // POS_SCALE: scale > 0, so the row maximum of scale*s is scale * max(s) and the
 // scaling folds into the exponent's FMA.  Otherwise every score is scaled first.
-template <int D, bool POS_SCALE, bool VARLEN>
+template <int D, bool POS_SCALE, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
+  constexpr bool VARLEN = MODE != kDense;  // queries packed by cu_seqlens
+  constexpr bool PAGED = MODE == kPaged;
   using T = Tile<D>;
   constexpr int S = kSlots;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
@@ -256,6 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   // even out the finishing times whatever the cost of each unit.
   constexpr int kXcd = kXcds;
   __shared__ int s_unit;  // the next unit, broadcast from thread 0
+  __shared__ int s_bad;   // paged: some wave met a block it cannot read
   const int G = gridDim.x;
   const int xcd = blockIdx.x % kXcd;
   int groups_before = 0;
@@ -278,10 +291,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   for (int e = 0; e < 2; ++e) {
     if (e == 1 && (VARLEN || !p.pairing || j == nq - 1 - j)) break;
     if (e == 1) __syncthreads();  // the first tile's O staging is done with the ring
+    if (PAGED && tid == 0) s_bad = 0;  // read by the previous item before the barrier above
     // this item: query tile qt of head h of sequence b, whose Nq query rows
     // start at token row q_tok0 and Nk key rows at k_tok0
     int b, h, qt, Nq, Nk;
     int64_t q_tok0, k_tok0, lse0;
+    bool bad = false;  // paged: a length or block id the kernel cannot read
     if constexpr (VARLEN) {
       // unit = (KV head, tile slot, query head within the group); the slots
       // of sequence s start at cu_q[s] / kBM + s, which leaves room for its
@@ -293,10 +308,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       b = find_seq(p.cu_q, p.n_seqs, p.total_q, slot, lane);
       const int q0 = clampi(p.cu_q[b], 0, p.total_q);
       const int q1 = clampi(p.cu_q[b + 1], q0, p.total_q);
-      const int k0 = clampi(p.cu_k[b], 0, p.total_k);
-      const int k1 = clampi(p.cu_k[b + 1], k0, p.total_k);
       Nq = q1 - q0;
-      Nk = k1 - k0;
+      int k0 = 0;
+      if constexpr (PAGED) {
+        // the chunk's queries are the last Nq of the sequence's seq_len tokens
+        const int len = p.seq_lens[b];
+        bad = len < 0 || len > p.max_blocks * kBlockTokens;
+        Nk = bad ? 0 : len;
+      } else {
+        k0 = clampi(p.cu_k[b], 0, p.total_k);
+        Nk = clampi(p.cu_k[b + 1], k0, p.total_k) - k0;
+      }
       const int off = slot - (q0 / kBM + b);
       const int ntl = (Nq + kBM - 1) / kBM;
       if (off < 0 || off >= ntl) {
@@ -347,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     // fetches logical piece c ^ swizzle(r) of key row r.
     const int64_t kv_row = (int64_t)p.Hkv * D;                 // elements between keys
     const uint32_t kv_row_b = static_cast<uint32_t>(kv_row * 2);
-    const int64_t head_off = k_tok0 * kv_row + (int64_t)hk * D;
+    const int64_t head_off = PAGED ? (int64_t)hk * D : k_tok0 * kv_row + (int64_t)hk * D;
     const uint16_t* kbase = p.k + head_off;
     const uint16_t* vbase = p.v + head_off;
     int koff[T::LPW], voff[T::LPW];
@@ -356,8 +378,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       const int pos = (wave * T::LPW + j) * 1024 + lane * 16;
       const int r = pos / T::ROWB;
       const int c = (pos % T::ROWB) >> 4;
-      koff[j] = r * (int)kv_row_b + ((c ^ T::kswz(r)) << 4);
-      voff[j] = r * (int)kv_row_b + ((c ^ T::vswz(r)) << 4);
+      // paged: the wave's rows (8 consecutive) lie in one cache block
+      const int rr = PAGED ? (r & (kBlockTokens - 1)) : r;
+      koff[j] = rr * (int)kv_row_b + ((c ^ T::kswz(r)) << 4);
+      voff[j] = rr * (int)kv_row_b + ((c ^ T::vswz(r)) << 4);
     }
     // Each wave issues the tiles of one kind in order (K(0), K(1), ... and
     // V(0), V(1), ...), so a running byte address per kind is enough; the range
@@ -372,10 +396,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     const uint8_t* knext = reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t_begin * tile_b;
     const uint8_t* vnext = reinterpret_cast<const uint8_t*>(vbase) + (int64_t)t_begin * tile_b;
     int kt = 0, vt = 0;  // index of the next tile of each kind
+    // Paged cache: this wave's 8 rows of a 64-key tile lie in logical block
+    // 4 t' + wave / 2 (t' = t_begin + t), rows 8 (wave % 2) .. +7 of it.  A
+    // block is looked up only when some of its keys exist (so the table is
+    // never read past the sequence); a needed id outside the pool marks the
+    // item bad and is not read.
+    static_assert(T::LPW * 1024 / T::ROWB == 8, "8 rows per wave and tile");
+    constexpr int kNone = INT_MIN;
+    const int* const trow = PAGED ? p.table + (int64_t)b * p.max_blocks : nullptr;
+    const int64_t blk_b = (int64_t)kBlockTokens * kv_row * 2;  // bytes per cache block
+    auto lookup = [&](int t) __attribute__((always_inline)) {
+      const int lb = (t_begin + t) * (T::BN / kBlockTokens) + (wave >> 1);
+      return (t < n_tiles && lb * kBlockTokens < Nk) ? trow[lb] : kNone;
+    };
+    auto paged_rsrc = [&](const uint16_t* base, int id, int t) __attribute__((always_inline)) {
+      const int lb = (t_begin + t) * (T::BN / kBlockTokens) + (wave >> 1);
+      const int nv = min(Nk - lb * kBlockTokens, kBlockTokens);  // keys in the block (> 0 if looked up)
+      const bool ok = id != kNone && (unsigned)id < (unsigned)p.num_blocks;
+      bad |= id != kNone && !ok;
+      const uint32_t bytes = ok ? (uint32_t)(nv - 1) * kv_row_b + T::ROWB : 0u;
+      return make_rsrc(reinterpret_cast<const uint8_t*>(base) + (ok ? (int64_t)id * blk_b : 0), bytes);
+    };
     auto issue = [&](auto DST, const uint8_t*& next, int& t, const int (&off)[T::LPW]) {
       constexpr uint32_t dst = decltype(DST)::value;
       const uint32_t bytes = t < n_tiles - 1 ? tile_b : (t == n_tiles - 1 ? last_b : 0u);
-      const i32x4 rsrc = make_rsrc(next, bytes);
+      i32x4 rsrc;
+      if constexpr (PAGED) {
+        const bool is_k = dst < S * T::TILEB;
+        rsrc = paged_rsrc(is_k ? kbase : vbase, lookup(t), t);
+      } else {
+        rsrc = make_rsrc(next, bytes);
+      }
       load_lds16<dst>(rsrc, off[0], lds_wave);
       if constexpr (T::LPW > 1) load_lds16<dst + 1024>(rsrc, off[1], lds_wave);
       static_assert(T::LPW <= 2, "load count per wave");
@@ -394,6 +445,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       issue(std::integral_constant<uint32_t, (S + decltype(SLOT)::value) * T::TILEB>{}, vnext, vt, voff);
     };
     using std::integral_constant;
+    // paged: buffer resources of the next M phase's K and V loads (K tile kt,
+    // V tile kt - 1), made at the start of each V phase from block ids looked
+    // up one phase earlier, so the scalar loads of the table never stall the
+    // matrix phase
+    i32x4 prk = {}, prv = {};
+    int id_k = kNone, id_next = kNone;  // ids of K tile kt - 1 and of tile kt
+    auto paged_advance = [&]() __attribute__((always_inline)) {
+      prv = paged_rsrc(vbase, id_k, kt - 1);
+      id_k = id_next;
+      prk = paged_rsrc(kbase, id_k, kt);
+      id_next = lookup(kt + 1);
+    };
 
     // ---- LDS fragment offsets (bytes from the LDS base, per lane; slots and
     // blocks are added as immediates)
@@ -480,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       static_assert(T::LPW == 1 || T::LPW == 2, "load count per wave");
       auto piece = [&](int j) __attribute__((always_inline)) {
         if (j == 0) {
-          rk = rsrc_of(knext, kt);
+          if constexpr (PAGED) rk = prk; else rk = rsrc_of(knext, kt);
           load_lds16<kdst>(rk, koff[0], lds_wave);
         }
         if (j == 1) {
@@ -489,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
           ++kt;
         }
         if (j == 2) {
-          rv = rsrc_of(vnext, vt);
+          if constexpr (PAGED) rv = prv; else rv = rsrc_of(vnext, vt);
           load_lds16<vdst>(rv, voff[0], lds_wave);
         }
         if (j == 3) {
@@ -597,6 +660,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     // V(k): softmax of tile k (mask, exponentials, occasional max update)
     auto v_phase = [&](auto U, int k, int vcase) __attribute__((always_inline)) {
       (void)U;
+      if constexpr (PAGED) paged_advance();
       if (vcase != 2) {
         if (vcase == 1) {
           const int j0 = (t_begin + k) * T::BN;
@@ -664,6 +728,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + (2 * S - 1) * T::TILEB + 16 * i) = u32x4{};
     unrolled_while<0, S - 1>([&](auto T_) { issue_k(T_); return true; });
     unrolled_while<0, S - 2>([&](auto T_) { issue_v(T_); return true; });
+    if constexpr (PAGED) {  // M(0) loads K tile S-1 and V tile S-2
+      id_k = lookup(kt - 1);
+      id_next = lookup(kt);
+      paged_advance();
+    }
     wait_vm<0>();  // also completes the Q loads, once, outside the loop
   #pragma unroll
     for (int c = 0; c < T::KC; ++c) asm volatile("" ::"v"(qf[c]));
@@ -687,8 +756,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     }
     if (!group_b) lds_barrier();  // A's extra barrier matches B's first one
     wait_vm<0>();  // loads past the last tile still land in LDS: drain them
+    if (PAGED && bad) s_bad = 1;
     // every wave's loads have landed before the next item's loads start
     __syncthreads();
+    if constexpr (PAGED) bad = s_bad != 0;
 
     // epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2.  O goes
     // through this wave's own LDS region (the ring is idle now), so that it
@@ -698,7 +769,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     float la = l_run, lb = l_run;
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(la), "+v"(lb));
     const float l_tot = la + lb;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (PAGED && bad) inv = __builtin_nanf("");  // O and LSE of the whole item are NaN
     constexpr int OPITCH = T::ROWB + 16;  // bytes per staged row
     static_assert(kWaves * kRowsPerWave * OPITCH <= T::LDS_BYTES, "O staging fits the ring");
     const uint32_t ostage = wave * kRowsPerWave * OPITCH;
@@ -727,8 +799,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     }
     const int row = qw0 + n;
     if (row < Nq && p.lse != nullptr && g == 0)
-      p.lse[lse0 + row] =
-          l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+      p.lse[lse0 + row] = (PAGED && bad) ? __builtin_nanf("")
+                          : l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
   // the O staging is done with the ring before the next unit's loads
   if (tid == 0) s_unit = first + grabbed;
@@ -756,7 +828,7 @@ namespace {
 
 // one persistent work group per CU (the LDS ring admits one per CU); launches
 // take scheduling-counter slots in turn
-template <bool VARLEN>
+template <int MODE>
 hipError_t launch(Params& p, int d, float scale, long long units, hipStream_t stream) {
   static std::atomic<unsigned> launches{0};
   p.slot = (int)(launches.fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
@@ -765,14 +837,14 @@ hipError_t launch(Params& p, int d, float scale, long long units, hipStream_t st
   const bool pos = scale > 0.f;
   if (d == 128) {
     if (pos)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, true, VARLEN>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, true, MODE>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, false, VARLEN>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, false, MODE>), grid, block, 0, stream, p);
   } else {
     if (pos)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, true, VARLEN>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, true, MODE>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, false, VARLEN>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, false, MODE>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -800,7 +872,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   // pair query tiles when there are enough pairs to fill the CUs
   const long long pairs = (long long)(p.total / p.n_qtiles) * ((p.n_qtiles + 1) / 2);
   p.pairing = pairs >= device_cus() ? 1 : 0;
-  return launch<false>(p, a.d, a.scale, p.pairing ? pairs : p.total, stream);
+  return launch<kDense>(p, a.d, a.scale, p.pairing ? pairs : p.total, stream);
 }
 
 long long fwd_bf16_varlen_grid(int n_seqs, int Hq, int total_q) {
@@ -830,7 +902,35 @@ hipError_t launch_fwd_bf16_varlen(const FwdVarlenArgs& a, hipStream_t stream) {
   p.pairing = 0;
   p.total = (int)fwd_bf16_varlen_grid(a.n_seqs, a.Hq, a.total_q);
   if (a.n_seqs == 0 || a.total_q == 0) return hipSuccess;
-  return launch<true>(p, a.d, a.scale, p.total, stream);
+  return launch<kVarlen>(p, a.d, a.scale, p.total, stream);
+}
+
+hipError_t launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream) {
+  Params p{};
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.kcache);
+  p.v = static_cast<const uint16_t*>(a.vcache);
+  p.o = static_cast<uint16_t*>(a.out);
+  p.lse = a.lse;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.group = a.Hq / a.Hkv;
+  p.causal = 1;
+  p.window = a.window;
+  p.sl2 = a.scale * kLog2e;
+  p.cu_q = a.cu_seqlens_q;
+  p.table = a.block_table;
+  p.seq_lens = a.seq_lens;
+  p.max_blocks = a.max_blocks_per_seq;
+  p.num_blocks = a.num_blocks;
+  p.n_seqs = a.n_seqs;
+  p.total_q = a.total_q;
+  p.vtiles = a.total_q / kBM + a.n_seqs;
+  p.n_qtiles = 1;
+  p.pairing = 0;
+  p.total = (int)fwd_bf16_varlen_grid(a.n_seqs, a.Hq, a.total_q);
+  if (a.n_seqs == 0 || a.total_q == 0) return hipSuccess;
+  return launch<kPaged>(p, a.d, a.scale, p.total, stream);
 }
 
 }  // namespace attn

@@ -47,6 +47,24 @@ hipError_t launch_fwd_bf16_varlen(const FwdVarlenArgs& a, hipStream_t stream);
 // Work units of the packed launch (for the size check).
 long long fwd_bf16_varlen_grid(int n_seqs, int Hq, int total_q);
 
+// Chunked prefill over a paged cache: sequence s owns query rows
+// [cu_seqlens_q[s], cu_seqlens_q[s+1]) of q/out, the last of its seq_lens[s]
+// cached tokens; caches are [num_blocks, 16, Hkv, d].
+struct PrefillPagedArgs {
+  const void* q;
+  const void* kcache;
+  const void* vcache;
+  const int* block_table;
+  const int* seq_lens;
+  const int* cu_seqlens_q;
+  void* out;
+  float* lse;
+  int n_seqs, total_q, Hq, Hkv, d, max_blocks_per_seq, num_blocks, window;
+  float scale;
+};
+
+hipError_t launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q;
   const void* kcache;

@@ -47,6 +47,12 @@ def varlen_fwd_flops(lens_q, lens_k, Hq: int, d: int, causal: bool, window: int)
     return 4.0 * d * pairs * Hq
 
 
+def prefill_paged_flops(seq_lens, chunks, Hq: int, d: int, window: int) -> float:
+    """Chunked prefill: each chunk's visible pairs against its sequence's cache."""
+    pairs = sum(visible_pairs(int(c), int(n), True, window) for n, c in zip(seq_lens, chunks))
+    return 4.0 * d * pairs * Hq
+
+
 def bwd_flops(B: int, Hq: int, Nq: int, Nk: int, d: int, causal: bool, window: int) -> float:
     """Algorithmic flops of the backward pass: five products the size of the
     forward's two (S recomputed, dP = dO V^T, dV, dK, dQ), i.e. 2.5x forward."""

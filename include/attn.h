@@ -14,6 +14,8 @@
  *                            only within itself;
  *   attn_decode_paged        one query per sequence over a block-paged KV
  *                            cache, split along the keys with a final merge;
+ *   attn_prefill_paged       several new tokens per sequence (a prefill
+ *                            chunk) over the same paged cache;
  *   attn_bwd                 the gradients of attn_fwd (bf16), recomputing
  *                            the probabilities from the saved log-sum-exp.
  *
@@ -179,6 +181,45 @@ int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
                       int B, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
                       int num_blocks, int window, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Chunked prefill over a block-paged KV cache ("Ch. 3: MHA Limitations, MQA,
+ * GQA, and FlashAttention": 3.1, new tokens attend to the cache after their
+ * own K/V are appended; the GQA code of 3.3 notes that a cache needs its own
+ * causal handling; "Inference Engineering", 2.5: the cache is split into
+ * blocks reached through a lookup table).  The kernel of attn_fwd reading
+ * K/V through the table.
+ *
+ *   q, out        [total_q, Hq, d] bf16: each sequence's new tokens back to back
+ *   cu_seqlens_q  [num_seqs + 1] int32 (device): sequence s owns rows
+ *                 cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 (nq_s rows)
+ *   kcache,
+ *   vcache        [num_blocks, block_size, Hkv, d] bf16, as for attn_decode_paged
+ *   block_table   [num_seqs, max_blocks_per_seq] int32 (device)
+ *   seq_lens      [num_seqs] int32 (device): cached tokens of sequence s, its
+ *                 new tokens included (they are the last nq_s of them)
+ *   lse           [Hq, total_q] float32, or NULL
+ *
+ * Always causal: new row i of sequence s sits at position seq_lens[s] - nq_s
+ * + i and sees the cached tokens up to it (the last `window` of them when
+ * window > 0).  Rows at negative positions (nq_s > seq_lens[s]) see no key
+ * and get O = 0, LSE = -inf.  A sequence whose length is negative or exceeds
+ * max_blocks_per_seq * block_size gets NaN in all its rows; a block id
+ * outside [0, num_blocks) that a 256-row query tile needs gets NaN in that
+ * tile's rows (a sequence of at most 256 new tokens without a window: all
+ * of them).  Nothing outside the pool, the used table entries and the given
+ * rows is read; rows of q outside every sequence are not written.  The cu
+ * array follows the rules of attn_fwd_varlen.
+ *
+ * block_size must be 16; d in {64, 128}; Hq % Hkv == 0; num_seqs *
+ * max_blocks_per_seq <= INT_MAX; Hq * (total_q / 256 + num_seqs) <= INT_MAX
+ * (ATTN_E_SHAPE otherwise).
+ */
+int attn_prefill_paged(const void* q, const void* kcache, const void* vcache,
+                       const int* block_table, const int* seq_lens, const int* cu_seqlens_q,
+                       void* out, float* lse, int num_seqs, int total_q, int Hq, int Hkv, int d,
+                       int block_size, int max_blocks_per_seq, int num_blocks, int window,
+                       float scale, void* stream);
 
 /*
  * Bytes of device workspace attn_bwd needs (two float32 values per query row

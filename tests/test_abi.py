@@ -149,3 +149,21 @@ def test_varlen_validation():
     # empty problems are no-ops whatever the pointers
     assert _varlen(ptr=None, cu=None, n=0) == _lib.ATTN_OK
     assert _varlen(ptr=None, cu=None, tq=0) == _lib.ATTN_OK
+
+
+def _prefill(ptr=1 << 20, n=3, tq=100, Hq=8, Hkv=2, d=128, bs=16, mb=8, nb=40, window=0):
+    return _lib.lib().attn_prefill_paged(ptr, ptr, ptr, ptr, ptr, ptr, ptr, None, n, tq, Hq,
+                                         Hkv, d, bs, mb, nb, window, 0.1, None)
+
+
+def test_prefill_paged_validation():
+    assert _prefill(ptr=None) == _lib.ATTN_E_NULL
+    assert _prefill(n=-1) == _lib.ATTN_E_SHAPE
+    assert _prefill(Hq=6, Hkv=4) == _lib.ATTN_E_SHAPE
+    assert _prefill(d=32) == _lib.ATTN_E_HEADDIM
+    assert _prefill(bs=32) == _lib.ATTN_E_SHAPE
+    assert _prefill(mb=0) == _lib.ATTN_E_SHAPE
+    assert _prefill(nb=0) == _lib.ATTN_E_SHAPE
+    assert _prefill(n=1 << 20, mb=1 << 12) == _lib.ATTN_E_SHAPE   # table entries
+    assert _prefill(ptr=None, n=0) == _lib.ATTN_OK
+    assert _prefill(ptr=None, tq=0) == _lib.ATTN_OK

@@ -46,6 +46,10 @@ __all__ = [
     "draw_lengths",
     "make_packed",
     "make_packed_config",
+    "PrefillPagedConfig",
+    "PREFILL_PAGED_CONFIGS",
+    "make_prefill_paged",
+    "make_prefill_paged_config",
 ]
 
 
@@ -140,6 +144,39 @@ PACKED_CONFIGS = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class PrefillPagedConfig:
+    """Chunked prefill: B sequences with cached contexts of len_lo..len_hi
+    tokens (the last ``chunk`` of them new) in a paged cache."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    len_lo: int
+    len_hi: int
+    chunk: int
+    window: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+# The paged decode batch (16 sequences of 8000..32000 cached tokens, 32 query
+# and 8 KV heads of 128, 16-token blocks) taking a 512-token prefill chunk
+# each instead of one token.
+PREFILL_PAGED_CONFIGS = {
+    "paged_prefill_16x32k_chunk512": PrefillPagedConfig("paged_prefill_16x32k_chunk512", 16,
+                                                        32, 8, 128, 16, 40000, 2000, 8000,
+                                                        32000, 512, 0, 7),
+}
+
+
 CHUNK_ROWS = 4096
 _THREADS = min(16, os.cpu_count() or 1)
 
@@ -231,6 +268,29 @@ def make_packed(lens_q, lens_k, Hq: int, Hkv: int, d: int, seed: int, dtype: str
 def make_packed_config(cfg: PackedConfig):
     lens = draw_lengths(cfg.total, cfg.mean_len, cfg.max_len, cfg.seed)
     return make_packed(lens, lens, cfg.Hq, cfg.Hkv, cfg.d, cfg.seed, "bf16")
+
+
+def make_prefill_paged(seq_lens, chunks, Hq: int, Hkv: int, d: int, block_size: int,
+                       num_blocks: int, max_blocks_per_seq: int, seed: int, poison: bool = True):
+    """A paged cache as ``make_paged`` (with the given lengths) plus the new
+    tokens' queries: q [sum(chunks), Hq, d] bf16 from tag 5 of ``seed`` and
+    cu_seqlens_q [B + 1] int32.  Returns a dict of CPU tensors."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    inp = make_paged(len(lens), Hq, Hkv, d, block_size, num_blocks, max_blocks_per_seq, seed,
+                     seq_lens=lens, poison=poison)
+    ch = np.asarray(chunks, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(ch)]).astype(np.int32)
+    inp["q"] = _to(draw_normal(seed, 5, (int(cu[-1]), Hq, d)), "bf16")
+    inp["cu_seqlens_q"] = torch.from_numpy(cu)
+    return inp
+
+
+def make_prefill_paged_config(cfg: PrefillPagedConfig, poison: bool = True):
+    rng = np.random.default_rng([cfg.seed, 6])
+    lens = rng.integers(cfg.len_lo, cfg.len_hi, size=cfg.B, endpoint=True)
+    chunks = np.minimum(lens, cfg.chunk)
+    return make_prefill_paged(lens, chunks, cfg.Hq, cfg.Hkv, cfg.d, cfg.block_size,
+                              cfg.num_blocks, cfg.max_blocks_per_seq, cfg.seed, poison)
 
 
 def make_paged(B: int, Hq: int, Hkv: int, d: int, block_size: int, num_blocks: int,
