@@ -27,7 +27,7 @@ from .attention import (attention, attention_head, decode_paged, gather_paged, p
                         visible_mask)
 from .online import online_softmax, tiled_attention_head, merge_states
 from .backward import attention_backward, attention_backward_head
-from .varlen import attention_varlen
+from .varlen import attention_varlen, attention_varlen_backward
 
 __all__ = [
     "attention",
@@ -42,4 +42,5 @@ __all__ = [
     "attention_backward",
     "attention_backward_head",
     "attention_varlen",
+    "attention_varlen_backward",
 ]

@@ -20,13 +20,16 @@ applied to each sequence's slice.  Readings (also in the design notes):
 
 Pinned by a pure-Python brute force over the whole packed axis with a
 segment mask (``oracle.brute.attention_brute_packed``), and by reductions to
-the dense oracle (``tests/test_oracle_varlen.py``).
+the dense oracle (``tests/test_oracle_varlen.py``).  The gradients are those
+of ``oracle.backward`` per sequence, pinned by finite differences of
+``attention_varlen`` itself.
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .attention import attention_head
+from .backward import attention_backward_head
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, causal: bool = False,
@@ -60,3 +63,38 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, causal: bo
             O[q0:q1, h, :] = o
             L[h, q0:q1] = l
     return O, L
+
+
+def attention_varlen_backward(q, k, v, do, cu_seqlens_q, cu_seqlens_k, scale=None,
+                              causal: bool = False, window: int = 0, heads=None):
+    """Gradients of sum(dO * O) for ``attention_varlen``.
+
+    Returns (dQ [total_q, Hq, d], dK [total_k, Hkv, d], dV [total_k, Hkv, dv],
+    D [Hq, total_q]) in float64; a KV head's gradients sum over the query
+    heads of its group.  Rows outside every sequence stay zero.  With
+    ``heads`` only those query heads are computed and added in.
+    """
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q).reshape(-1)]
+    ck = [int(x) for x in np.asarray(cu_seqlens_k).reshape(-1)]
+    dQ = np.zeros((total_q, Hq, d))
+    dK = np.zeros((total_k, Hkv, d))
+    dV = np.zeros((total_k, Hkv, v.shape[2]))
+    Ds = np.zeros((Hq, total_q))
+    for s in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[s], cq[s + 1], ck[s], ck[s + 1]
+        for h in (range(Hq) if heads is None else heads):
+            hk = h // G
+            dq, dk, dv, D = attention_backward_head(q[q0:q1, h, :], k[k0:k1, hk, :],
+                                                    v[k0:k1, hk, :], do[q0:q1, h, :], scale,
+                                                    causal, window)
+            dQ[q0:q1, h] = dq
+            dK[k0:k1, hk] += dk
+            dV[k0:k1, hk] += dv
+            Ds[h, q0:q1] = D
+    return dQ, dK, dV, Ds
+
