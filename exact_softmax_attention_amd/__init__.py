@@ -13,6 +13,7 @@ computation runs in the library's HIP kernels; there is no fallback.
     attn_prefill_paged(q, kcache, vcache, block_table, seq_lens, cu_seqlens_q, ...)
     attn_bwd(q, k, v, out, dout, lse, causal=False, window=0, scale=None)
     attn_bwd_workspace_size(B, Hq, Nq)
+    attn_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, ...)
     attn_status_str(code)
 
 Layouts: q [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d]; out like q; lse [B, Hq, Nq]
@@ -38,6 +39,7 @@ __all__ = [
     "attn_prefill_paged",
     "attn_bwd",
     "attn_bwd_workspace_size",
+    "attn_bwd_varlen",
     "attn_status_str",
     "AttnError",
 ]
@@ -309,4 +311,52 @@ def attn_bwd(q, k, v, out, dout, lse, causal: bool = False, window: int = 0, sca
         B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), int(window), float(scale),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
+                    window: int = 0, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """bf16 backward of attn_fwd_varlen (packed sequences).  Returns (dq, dk, dv)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _dev(t, name, torch.bfloat16)
+    _dev(lse, "lse", torch.float32)
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("expected q [total_q,Hq,d], k and v [total_k,Hkv,d]")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have q's shape")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk_ = k.shape
+    if dk_ != d:
+        raise ValueError("q and k disagree on the head dimension")
+    if lse.shape != (Hq, total_q):
+        raise ValueError("lse must be [Hq, total_q]")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape or \
+            cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be [num_seqs + 1]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for t, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if t is None:
+            t = torch.empty_like(like)
+        else:
+            _dev(t, name, torch.bfloat16)
+            if t.shape != like.shape:
+                raise ValueError(f"{name} has the wrong shape")
+        outs.append(t)
+    dq, dk, dv = outs
+    need = attn_bwd_workspace_size(1, Hq, total_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device.type != "cuda":
+        raise ValueError("workspace must be on the GPU")
+    code = _lib.lib().attn_bwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
+        cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1, total_q, total_k, Hq, Hkv, d,
+        int(bool(causal)), int(window), float(scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(code, "attn_bwd_varlen")
     return dq, dk, dv

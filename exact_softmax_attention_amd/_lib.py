@@ -36,6 +36,8 @@ SIGNATURES = {
     "attn_bwd_workspace_size": (_SZ, [_I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                       _P, _SZ, _P]),
+    "attn_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                             _I, _I, _F, _P, _SZ, _P]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
 }
 

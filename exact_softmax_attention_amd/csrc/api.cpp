@@ -132,6 +132,37 @@ int attn_prefill_paged(const void* q, const void* kcache, const void* vcache,
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs, int total_q,
+                    int total_k, int Hq, int Hkv, int d, int causal, int window, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || total_k < 0) return ATTN_E_SHAPE;
+  const int st = check_common(num_seqs, Hq, Hkv, d);
+  if (st != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return ATTN_E_MASK;
+  if (window > 0 && !causal) return ATTN_E_MASK;
+  if (Hq > 65535) return ATTN_E_SHAPE;  // grid y
+  // schedule slots of both packed axes fit the grid's x dimension
+  if ((long long)total_q / 128 + num_seqs > INT_MAX || (long long)total_k / 128 + num_seqs > INT_MAX)
+    return ATTN_E_SHAPE;
+  if ((long long)total_q * Hq * d > (1LL << 40) || (long long)Hkv * d > (1LL << 22))
+    return ATTN_E_SHAPE;
+  if (num_seqs == 0 || (total_q == 0 && total_k == 0)) return ATTN_OK;
+  if (!cu_seqlens_q || !cu_seqlens_k) return ATTN_E_NULL;
+  if (total_q > 0 && (!q || !out || !dout || !lse || !dq)) return ATTN_E_NULL;
+  if (total_k > 0 && (!k || !v || !dk || !dv)) return ATTN_E_NULL;
+  const size_t need = attn::bwd_workspace_bytes(1, Hq, total_q);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_E_WORKSPACE;
+  attn::BwdVarlenArgs a{q,        k,        v,          out,          dout,
+                        lse,      dq,       dk,         dv,           cu_seqlens_q,
+                        cu_seqlens_k, num_seqs, total_q, total_k,    Hq,
+                        Hkv,      d,        causal,     window > 0 ? window : 0,
+                        scale,    workspace};
+  const hipError_t e = attn::launch_bwd_bf16_varlen(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
 size_t attn_decode_paged_workspace_size(int B, int Hq, int d, int block_size,
                                         int max_blocks_per_seq) {
   if (B < 0 || Hq < 1 || (d != 64 && d != 128) || block_size != 16 || max_blocks_per_seq < 1)

@@ -75,11 +75,57 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dsum;   // [B, Hq, Nq]: D = rowsum(dO * O)
-  float* lse2;   // [B, Hq, Nq]: LSE * log2(e), +inf for a row without keys
+  float* dsum;   // [B, Hq, Nq] ([Hq, total_q] packed): D = rowsum(dO * O)
+  float* lse2;   // same layout: LSE * log2(e), +inf for a row without keys
   int B, Hq, Hkv, group, Nq, Nk, causal, window;
   float scale, sl2;
+  // packed sequences: sequence s owns query rows [cu_q[s], cu_q[s+1]) and key
+  // rows [cu_k[s], cu_k[s+1]); LSE, D and lse2 are [Hq, total_q]
+  const int* cu_q;
+  const int* cu_k;
+  int n_seqs, total_q, total_k;
 };
+
+// The sequence and 128-row tile of a work group.  Dense: sequence blockIdx.z,
+// tile blockIdx.x.  Packed: blockIdx.x is a slot of the packed axis (queries
+// or keys, `cu` and `total`), the slots of sequence s starting at
+// cu[s] / 128 + s; tile < 0 for a slot past the sequence's tiles.
+struct SeqTile {
+  int b, tile, Nq, Nk;
+  int64_t q0, k0;  // first query and key row of the sequence
+  __device__ int64_t stat(const BwdParams& p, int h, bool packed) const {  // LSE index of row 0
+    return packed ? (int64_t)h * p.total_q + q0 : ((int64_t)b * p.Hq + h) * Nq;
+  }
+};
+
+template <bool VARLEN>
+__device__ __forceinline__ SeqTile seq_tile(const BwdParams& p, const int* cu, int total,
+                                            int lane) {
+  SeqTile t;
+  if constexpr (VARLEN) {
+    constexpr int TILE = kBwdWaves * kBlk;
+    const int slot = blockIdx.x;
+    t.b = find_seq<TILE>(cu, p.n_seqs, total, slot, lane);
+    const int q0 = clampi(p.cu_q[t.b], 0, p.total_q);
+    const int k0 = clampi(p.cu_k[t.b], 0, p.total_k);
+    t.Nq = clampi(p.cu_q[t.b + 1], q0, p.total_q) - q0;
+    t.Nk = clampi(p.cu_k[t.b + 1], k0, p.total_k) - k0;
+    t.q0 = q0;
+    t.k0 = k0;
+    const int a0 = clampi(cu[t.b], 0, total);
+    const int len = cu == p.cu_q ? t.Nq : t.Nk;
+    const int off = slot - (a0 / TILE + t.b);
+    t.tile = (off >= 0 && off * TILE < len) ? off : -1;
+  } else {
+    t.b = blockIdx.z;
+    t.tile = blockIdx.x;
+    t.Nq = p.Nq;
+    t.Nk = p.Nk;
+    t.q0 = (int64_t)t.b * p.Nq;
+    t.k0 = (int64_t)t.b * p.Nk;
+  }
+  return t;
+}
 
 template <int D>
 struct BT {
@@ -163,13 +209,14 @@ __device__ __forceinline__ bf16x8 tr_frag(const lds_u8* lds, uint32_t off, int l
 // ---------------------------------------------------------------------------
 // D and LSE * log2(e) per row.
 
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
   constexpr int LPR = D / 8;          // lanes per row (16 bytes each)
   constexpr int RPB = 256 / LPR;      // rows per block step
   const int tid = threadIdx.x;
   const int sub = tid % LPR;
-  const int64_t rows = (int64_t)p.B * p.Nq * p.Hq;  // rows in [B, Nq, Hq] order
+  // rows in [B, Nq, Hq] (packed: [total_q, Hq]) order
+  const int64_t rows = VARLEN ? (int64_t)p.total_q * p.Hq : (int64_t)p.B * p.Nq * p.Hq;
   for (int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR; r < rows; r += (int64_t)gridDim.x * RPB) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(p.dout + r * D + sub * 8);
     const u32x4 b = *reinterpret_cast<const u32x4*>(p.o + r * D + sub * 8);
@@ -182,9 +229,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
     if (sub == 0) {
       const int h = (int)(r % p.Hq);
       const int64_t bi = r / p.Hq;
-      const int i = (int)(bi % p.Nq);
-      const int b = (int)(bi / p.Nq);
-      const int64_t o = ((int64_t)b * p.Hq + h) * p.Nq + i;
+      int64_t o;
+      if constexpr (VARLEN) {
+        o = (int64_t)h * p.total_q + bi;
+      } else {
+        const int i = (int)(bi % p.Nq);
+        const int b = (int)(bi / p.Nq);
+        o = ((int64_t)b * p.Hq + h) * p.Nq + i;
+      }
       const float l = p.lse[o];
       p.dsum[o] = s;
       p.lse2[o] = l == kNegInf ? __builtin_inff() : l * kLog2e;
@@ -195,7 +247,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV.
 
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p) {
   using T = BT<D>;
   constexpr int QTILE = T::PITCH * kBlk;  // bytes of one staged 32-row tile
@@ -206,23 +258,26 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const SeqTile sq = seq_tile<VARLEN>(p, p.cu_k, p.total_k, lane);
+  if (sq.tile < 0) return;  // a schedule slot past the sequence (whole group)
+  const int Nq = sq.Nq, Nk = sq.Nk;
+  const int kt = sq.tile, hk = blockIdx.y;
   const int k0 = kt * kBwdWaves * kBlk;          // first key of the tile
   const int kw0 = k0 + wave * kBlk;              // first key of this wave
   const int key = kw0 + (lane & 31);             // this lane's key (column)
   const int g = lane >> 5;
-  const int delta = p.Nk - p.Nq;
+  const int delta = Nk - Nq;
   const int64_t kv_row = (int64_t)p.Hkv * D;
   const int64_t q_row = (int64_t)p.Hq * D;
 
   // K and V of the lane's key as B operands (features 16c + 8g .. +7)
   bf16x8 kb[T::KC], vb[T::KC];
   {
-    const int64_t off = ((int64_t)b * p.Nk + key) * kv_row + (int64_t)hk * D + 8 * g;
+    const int64_t off = (sq.k0 + key) * kv_row + (int64_t)hk * D + 8 * g;
 #pragma unroll
     for (int c = 0; c < T::KC; ++c) {
       u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (key < p.Nk) {
+      if (key < Nk) {
         x = *reinterpret_cast<const u32x4*>(p.k + off + 16 * c);
         y = *reinterpret_cast<const u32x4*>(p.v + off + 16 * c);
       }
@@ -235,10 +290,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
   for (int db = 0; db < T::NDB; ++db) dkt[db] = dvt[db] = f32x16{};
 
   // query rows that see some key of the tile: [qlo, qhi)
-  const int klast = min(p.Nk, k0 + kBwdWaves * kBlk) - 1;
-  int qlo = 0, qhi = p.Nq;
+  const int klast = min(Nk, k0 + kBwdWaves * kBlk) - 1;
+  int qlo = 0, qhi = Nq;
   if (p.causal) qlo = max(0, k0 - delta);
-  if (p.window > 0) qhi = min(p.Nq, klast - delta + p.window);
+  if (p.window > 0) qhi = min(Nq, klast - delta + p.window);
   const int nblk = qhi > qlo ? (qhi - (qlo & ~(kBlk - 1)) + kBlk - 1) / kBlk : 0;
   const int q_first = qlo & ~(kBlk - 1);
   const int steps = nblk * p.group;  // (head, block) pairs, head-major
@@ -255,15 +310,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
     if (s >= steps) return;
     const int h = hk * p.group + s / nblk;
     const int i0 = q_first + (s % nblk) * kBlk;
-    const uint16_t* qb = p.q + (int64_t)b * p.Nq * q_row + (int64_t)h * D;
-    const uint16_t* ob = p.dout + (int64_t)b * p.Nq * q_row + (int64_t)h * D;
-    st.q.load(qb, q_row, i0, p.Nq, so);
-    st.o.load(ob, q_row, i0, p.Nq, so);
+    const uint16_t* qb = p.q + sq.q0 * q_row + (int64_t)h * D;
+    const uint16_t* ob = p.dout + sq.q0 * q_row + (int64_t)h * D;
+    st.q.load(qb, q_row, i0, Nq, so);
+    st.o.load(ob, q_row, i0, Nq, so);
     if (tid < kBlk) {
       const int i = i0 + tid;
-      const int64_t o = ((int64_t)b * p.Hq + h) * p.Nq + i;
-      st.l2 = i < p.Nq ? p.lse2[o] : __builtin_inff();
-      st.d = i < p.Nq ? p.dsum[o] : 0.f;
+      const int64_t o = sq.stat(p, h, VARLEN) + i;
+      st.l2 = i < Nq ? p.lse2[o] : __builtin_inff();
+      st.d = i < Nq ? p.dsum[o] : 0.f;
     }
   };
   auto stash = [&](const Set& st, int buf) __attribute__((always_inline)) {
@@ -291,7 +346,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
     const uint32_t qoff = (2 * buf) * QTILE, ooff = (2 * buf + 1) * QTILE;
     const uint32_t loff = stat0 + (2 * buf) * kBlk * 4, doff = stat0 + (2 * buf + 1) * kBlk * 4;
     // does this wave's 32 x 32 block hold any visible pair, and does it need a mask?
-    bool any = kw0 < p.Nk;
+    bool any = kw0 < Nk;
     if (p.causal && kw0 > i0 + kBlk - 1 + delta) any = false;
     if (p.window > 0 && i0 + delta - (kw0 + kBlk - 1) >= p.window) any = false;
     const bool full = (!p.causal || kw0 + kBlk - 1 <= i0 + delta) &&
@@ -360,8 +415,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds key `key`, features
   // 32 db + 8 t + 4 g .. +3 in registers 4 t .. 4 t + 3.
-  if (key < p.Nk) {
-    const int64_t off = ((int64_t)b * p.Nk + key) * kv_row + (int64_t)hk * D;
+  if (key < Nk) {
+    const int64_t off = (sq.k0 + key) * kv_row + (int64_t)hk * D;
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
@@ -381,7 +436,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
 // ---------------------------------------------------------------------------
 // dQ.
 
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) {
   using T = BT<D>;
   constexpr int KN = 64;                  // keys per step (two 32-key blocks)
@@ -391,32 +446,35 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SeqTile sq = seq_tile<VARLEN>(p, p.cu_q, p.total_q, lane);
+  if (sq.tile < 0) return;  // a schedule slot past the sequence (whole group)
+  const int Nq = sq.Nq, Nk = sq.Nk;
+  const int qt = sq.tile, h = blockIdx.y;
   const int hk = h / p.group;
   const int q0 = qt * kBwdWaves * kBlk;
   const int qw0 = q0 + wave * kBlk;
   const int row = qw0 + (lane & 31);       // this lane's query row (column of S^T)
   const int g = lane >> 5;
-  const int delta = p.Nk - p.Nq;
+  const int delta = Nk - Nq;
   const int64_t kv_row = (int64_t)p.Hkv * D;
   const int64_t q_row = (int64_t)p.Hq * D;
 
   bf16x8 qb[T::KC], ob[T::KC];
   float l2 = __builtin_inff(), dd = 0.f;
   {
-    const int64_t off = ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D + 8 * g;
+    const int64_t off = (sq.q0 + row) * q_row + (int64_t)h * D + 8 * g;
 #pragma unroll
     for (int c = 0; c < T::KC; ++c) {
       u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (row < p.Nq) {
+      if (row < Nq) {
         x = *reinterpret_cast<const u32x4*>(p.q + off + 16 * c);
         y = *reinterpret_cast<const u32x4*>(p.dout + off + 16 * c);
       }
       qb[c] = __builtin_bit_cast(bf16x8, x);
       ob[c] = __builtin_bit_cast(bf16x8, y);
     }
-    if (row < p.Nq) {
-      const int64_t o = ((int64_t)b * p.Hq + h) * p.Nq + row;
+    if (row < Nq) {
+      const int64_t o = sq.stat(p, h, VARLEN) + row;
       l2 = p.lse2[o];
       dd = p.dsum[o];
     }
@@ -426,9 +484,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) 
   for (int db = 0; db < T::NDB; ++db) dqt[db] = f32x16{};
 
   // keys some row of the tile sees: [jlo, jhi)
-  const int qlast = min(p.Nq, q0 + kBwdWaves * kBlk) - 1;
-  int jlo = 0, jhi = p.Nk;
-  if (p.causal) jhi = min(p.Nk, qlast + delta + 1);
+  const int qlast = min(Nq, q0 + kBwdWaves * kBlk) - 1;
+  int jlo = 0, jhi = Nk;
+  if (p.causal) jhi = min(Nk, qlast + delta + 1);
   if (p.window > 0) jlo = max(0, q0 + delta - p.window + 1);
   const int j_first = jlo & ~(KN - 1);
   const int steps = jhi > j_first ? (jhi - j_first + KN - 1) / KN : 0;
@@ -439,13 +497,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) 
     Stage<D, KN> k, v;
   };
   Set sets[kAhead];
-  const uint16_t* kbase = p.k + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
-  const uint16_t* vbase = p.v + (int64_t)b * p.Nk * kv_row + (int64_t)hk * D;
+  const uint16_t* kbase = p.k + sq.k0 * kv_row + (int64_t)hk * D;
+  const uint16_t* vbase = p.v + sq.k0 * kv_row + (int64_t)hk * D;
   const StageOff<D, KN> so(kv_row, tid);
   auto fetch = [&](Set& st, int s) __attribute__((always_inline)) {
     if (s >= steps) return;
-    st.k.load(kbase, kv_row, j_first + s * KN, p.Nk, so);
-    st.v.load(vbase, kv_row, j_first + s * KN, p.Nk, so);
+    st.k.load(kbase, kv_row, j_first + s * KN, Nk, so);
+    st.v.load(vbase, kv_row, j_first + s * KN, Nk, so);
   };
   auto stash = [&](const Set& st, int buf) __attribute__((always_inline)) {
     st.k.store(lds, (2 * buf) * KTILE, tid);
@@ -468,7 +526,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) 
 #pragma unroll
     for (int kb2 = 0; kb2 < KN / kBlk; ++kb2) {
       const int jb = j0 + kb2 * kBlk;  // first key of the 32-key block
-      bool any = qw0 < p.Nq && jb < p.Nk;
+      bool any = qw0 < Nq && jb < Nk;
       if (p.causal && jb > qw0 + kBlk - 1 + delta) any = false;
       if (p.window > 0 && qw0 + delta - (jb + kBlk - 1) >= p.window) any = false;
       const bool full = (!p.causal || jb + kBlk - 1 <= qw0 + delta) &&
@@ -523,8 +581,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) 
    if (!more) break;
   }
 
-  if (row < p.Nq) {
-    const int64_t off = ((int64_t)b * p.Nq + row) * q_row + (int64_t)h * D;
+  if (row < Nq) {
+    const int64_t off = (sq.q0 + row) * q_row + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
@@ -545,59 +603,93 @@ size_t bwd_workspace_bytes(int B, int Hq, int Nq) {
   return 2 * ((n * sizeof(float) + 255) / 256 * 256);
 }
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
-  BwdParams p;
-  p.q = static_cast<const uint16_t*>(a.q);
-  p.k = static_cast<const uint16_t*>(a.k);
-  p.v = static_cast<const uint16_t*>(a.v);
-  p.o = static_cast<const uint16_t*>(a.out);
-  p.dout = static_cast<const uint16_t*>(a.dout);
-  p.lse = a.lse;
-  p.dq = static_cast<uint16_t*>(a.dq);
-  p.dk = static_cast<uint16_t*>(a.dk);
-  p.dv = static_cast<uint16_t*>(a.dv);
-  const size_t n = (size_t)a.B * a.Hq * a.Nq;
-  char* ws = static_cast<char*>(a.workspace);
-  p.dsum = reinterpret_cast<float*>(ws);
-  p.lse2 = reinterpret_cast<float*>(ws + (n * sizeof(float) + 255) / 256 * 256);
-  p.B = a.B;
-  p.Hq = a.Hq;
-  p.Hkv = a.Hkv;
-  p.group = a.Hq / a.Hkv;
-  p.Nq = a.Nq;
-  p.Nk = a.Nk;
-  p.causal = a.causal;
-  p.window = a.window;
-  p.scale = a.scale;
-  p.sl2 = a.scale * kLog2e;
+namespace {
 
-  const long long rows = (long long)a.B * a.Nq * a.Hq;
-  const int rpb = 256 / (a.d / 8);
+// the three kernels in order; an empty grid is not launched (with no query
+// rows the dK/dV kernel still writes zeros, with no keys the dQ kernel does)
+template <bool VARLEN>
+hipError_t launch_bwd(const BwdParams& p, int d, long long rows, dim3 g1, dim3 g2,
+                      hipStream_t stream) {
+  const int rpb = 256 / (d / 8);
   const long long nb = (rows + rpb - 1) / rpb;
   const dim3 g0((unsigned)(nb < 65536 ? nb : 65536));
-  const dim3 g1((a.Nk + kBwdWaves * kBlk - 1) / (kBwdWaves * kBlk), a.Hkv, a.B);
-  const dim3 g2((a.Nq + kBwdWaves * kBlk - 1) / (kBwdWaves * kBlk), a.Hq, a.B);
-  // an empty grid is not launched: with Nq = 0 the dK/dV kernel still writes
-  // zeros, with Nk = 0 the dQ kernel does
   if (rows > 0) {
-    if (a.d == 128)
-      hipLaunchKernelGGL(bwd_prep_kernel<128>, g0, dim3(256), 0, stream, p);
+    if (d == 128)
+      hipLaunchKernelGGL((bwd_prep_kernel<128, VARLEN>), g0, dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL(bwd_prep_kernel<64>, g0, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((bwd_prep_kernel<64, VARLEN>), g0, dim3(256), 0, stream, p);
   }
   if ((long long)g1.x * g1.y * g1.z > 0) {
-    if (a.d == 128)
-      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, g1, dim3(kBwdThreads), 0, stream, p);
+    if (d == 128)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, VARLEN>), g1, dim3(kBwdThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, g1, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, VARLEN>), g1, dim3(kBwdThreads), 0, stream, p);
   }
   if ((long long)g2.x * g2.y * g2.z > 0) {
-    if (a.d == 128)
-      hipLaunchKernelGGL(bwd_dq_kernel<128>, g2, dim3(kBwdThreads), 0, stream, p);
+    if (d == 128)
+      hipLaunchKernelGGL((bwd_dq_kernel<128, VARLEN>), g2, dim3(kBwdThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL(bwd_dq_kernel<64>, g2, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<64, VARLEN>), g2, dim3(kBwdThreads), 0, stream, p);
   }
   return hipGetLastError();
+}
+
+BwdParams common_params(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        int Hq, int Hkv, int causal, int window, float scale, void* workspace,
+                        size_t stat_rows) {
+  BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(out);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  char* ws = static_cast<char*>(workspace);
+  p.dsum = reinterpret_cast<float*>(ws);
+  p.lse2 = reinterpret_cast<float*>(ws + (stat_rows * sizeof(float) + 255) / 256 * 256);
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.causal = causal;
+  p.window = window;
+  p.scale = scale;
+  p.sl2 = scale * kLog2e;
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p = common_params(a.q, a.k, a.v, a.out, a.dout, a.lse, a.dq, a.dk, a.dv, a.Hq,
+                              a.Hkv, a.causal, a.window, a.scale, a.workspace,
+                              (size_t)a.B * a.Hq * a.Nq);
+  p.B = a.B;
+  p.Nq = a.Nq;
+  p.Nk = a.Nk;
+  constexpr int TILE = kBwdWaves * kBlk;
+  const dim3 g1((a.Nk + TILE - 1) / TILE, a.Hkv, a.B);
+  const dim3 g2((a.Nq + TILE - 1) / TILE, a.Hq, a.B);
+  return launch_bwd<false>(p, a.d, (long long)a.B * a.Nq * a.Hq, g1, g2, stream);
+}
+
+hipError_t launch_bwd_bf16_varlen(const BwdVarlenArgs& a, hipStream_t stream) {
+  BwdParams p = common_params(a.q, a.k, a.v, a.out, a.dout, a.lse, a.dq, a.dk, a.dv, a.Hq,
+                              a.Hkv, a.causal, a.window, a.scale, a.workspace,
+                              (size_t)a.Hq * a.total_q);
+  p.cu_q = a.cu_seqlens_q;
+  p.cu_k = a.cu_seqlens_k;
+  p.n_seqs = a.n_seqs;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
+  p.B = 1;
+  constexpr int TILE = kBwdWaves * kBlk;
+  const dim3 g1(a.n_seqs > 0 ? a.total_k / TILE + a.n_seqs : 0, a.Hkv, 1);
+  const dim3 g2(a.n_seqs > 0 ? a.total_q / TILE + a.n_seqs : 0, a.Hq, 1);
+  return launch_bwd<true>(p, a.d, (long long)a.total_q * a.Hq, g1, g2, stream);
 }
 
 }  // namespace attn

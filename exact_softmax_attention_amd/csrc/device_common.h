@@ -71,4 +71,28 @@ constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppRor8 = 0x128;
 
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+// Packed sequences: the sequence whose schedule slots hold slot v, i.e. the
+// largest s in [0, n) with start(s) = cu[s] / TILE + s <= v (start is strictly
+// increasing for nondecreasing cu; cu is clamped to [0, total] as read).  A
+// 64-way search: each round the wave's lanes test 64 evenly spaced
+// candidates and the count of passing lanes narrows the range 64-fold.  The
+// result stays in [0, n) whatever cu holds.  A sequence's TILE-row tiles
+// fit in its slots: start(s + 1) - start(s) >= ceil(len(s) / TILE).
+template <int TILE>
+__device__ __forceinline__ int find_seq(const int* cu, int n, int total, int v, int lane) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    bool pass = false;
+    if (idx < hi) pass = clampi(cu[idx], 0, total) / TILE + idx <= v;
+    const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(pass));
+    lo += (max(cnt, 1) - 1) * step;
+    hi = min(hi, lo + step);
+  }
+  return __builtin_amdgcn_readfirstlane(lo);
+}
+
 }  // namespace attn

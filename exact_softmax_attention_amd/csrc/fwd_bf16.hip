@@ -177,27 +177,6 @@ __device__ __forceinline__ int floordiv(int a, int b) {  // b > 0
   return (a % b != 0 && a < 0) ? q - 1 : q;
 }
 
-__device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
-
-// Packed sequences: the sequence whose schedule slots hold slot v, i.e. the
-// largest s in [0, n) with start(s) = cu[s] / kBM + s <= v (start is strictly
-// increasing for nondecreasing cu; cu is clamped to [0, total] as read).  A
-// 64-way search: each round the wave's lanes test 64 evenly spaced
-// candidates and the count of passing lanes narrows the range 64-fold.  The
-// result stays in [0, n) whatever cu holds.
-__device__ __forceinline__ int find_seq(const int* cu, int n, int total, int v, int lane) {
-  int lo = 0, hi = n;
-  while (hi - lo > 1) {
-    const int step = (hi - lo + 63) / 64;
-    const int idx = lo + lane * step;
-    bool pass = false;
-    if (idx < hi) pass = clampi(cu[idx], 0, total) / kBM + idx <= v;
-    const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(pass));
-    lo += (max(cnt, 1) - 1) * step;
-    hi = min(hi, lo + step);
-  }
-  return __builtin_amdgcn_readfirstlane(lo);
-}
 
 template <int I, int N, typename F>
 __device__ __forceinline__ bool unrolled_while(F&& f) {
@@ -305,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       const int rest = unit / p.group;
       const int slot = rest % p.vtiles;
       h = (rest / p.vtiles) * p.group + hg;
-      b = find_seq(p.cu_q, p.n_seqs, p.total_q, slot, lane);
+      b = find_seq<kBM>(p.cu_q, p.n_seqs, p.total_q, slot, lane);
       const int q0 = clampi(p.cu_q[b], 0, p.total_q);
       const int q1 = clampi(p.cu_q[b + 1], q0, p.total_q);
       Nq = q1 - q0;

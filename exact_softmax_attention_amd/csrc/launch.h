@@ -97,6 +97,28 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int B, int Hq, int Nq);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
+// Gradients of the packed-sequence forward (layouts of FwdVarlenArgs; the
+// workspace is bwd_workspace_bytes(1, Hq, total_q)).
+struct BwdVarlenArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int* cu_seqlens_q;
+  const int* cu_seqlens_k;
+  int n_seqs, total_q, total_k, Hq, Hkv, d;
+  int causal, window;
+  float scale;
+  void* workspace;
+};
+
+hipError_t launch_bwd_bf16_varlen(const BwdVarlenArgs& a, hipStream_t stream);
+
 size_t decode_workspace_bytes(int B, int Hq, int d, int block_size, int max_blocks_per_seq);
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
 

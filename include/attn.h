@@ -17,7 +17,8 @@
  *   attn_prefill_paged       several new tokens per sequence (a prefill
  *                            chunk) over the same paged cache;
  *   attn_bwd                 the gradients of attn_fwd (bf16), recomputing
- *                            the probabilities from the saved log-sum-exp.
+ *                            the probabilities from the saved log-sum-exp;
+ *   attn_bwd_varlen          the gradients of attn_fwd_varlen.
  *
  * Sources (pages; section names as printed):
  *   - "Attention Is O(n^2): FlashAttention vs Linear Attention", "Why
@@ -259,6 +260,30 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
 
 /* Static, human-readable text for a status code. */
 const char* attn_status_str(int status);
+
+/*
+ * Gradients of attn_fwd_varlen (packed sequences; "How to Reduce Attention
+ * Computation Cost in LLM Training" counts packing among the main savings of
+ * training, which needs this backward).  The same three kernels as attn_bwd,
+ * scheduled over each sequence's 128-row tiles.
+ *
+ *   q, out, dout, dq  [total_q, Hq, d] bf16;  k, v, dk, dv [total_k, Hkv, d] bf16
+ *   lse               [Hq, total_q] float32 from attn_fwd_varlen (required)
+ *   cu_seqlens_q/_k   as for attn_fwd_varlen (device int32, num_seqs + 1)
+ *   workspace         attn_bwd_workspace_size(1, Hq, total_q) bytes of device memory
+ *
+ * Each sequence's gradients are those of its own attention (masks and
+ * bottom-right alignment within the sequence); a sequence with no query rows
+ * gets dK = dV = 0, one with no keys dQ = 0.  Rows outside every sequence are
+ * not written.  Sizes and masks as for attn_fwd_varlen, plus Hq <= 65535 and
+ * total_q * Hq * d <= 2^40 (ATTN_E_SHAPE); ATTN_E_WORKSPACE for a missing or
+ * short workspace.
+ */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                    int total_q, int total_k, int Hq, int Hkv, int d, int causal, int window,
+                    float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -167,3 +167,21 @@ def test_prefill_paged_validation():
     assert _prefill(n=1 << 20, mb=1 << 12) == _lib.ATTN_E_SHAPE   # table entries
     assert _prefill(ptr=None, n=0) == _lib.ATTN_OK
     assert _prefill(ptr=None, tq=0) == _lib.ATTN_OK
+
+
+def _bwdv(ptr=1 << 20, n=2, tq=300, tk=300, Hq=4, Hkv=2, d=128, causal=1, window=0, ws=1 << 22,
+          ws_bytes=1 << 20):
+    return _lib.lib().attn_bwd_varlen(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, n,
+                                      tq, tk, Hq, Hkv, d, causal, window, 0.1, ws, ws_bytes, None)
+
+
+def test_bwd_varlen_validation():
+    assert _bwdv(ptr=None) == _lib.ATTN_E_NULL
+    assert _bwdv(n=-1) == _lib.ATTN_E_SHAPE
+    assert _bwdv(Hq=3, Hkv=2) == _lib.ATTN_E_SHAPE
+    assert _bwdv(d=96) == _lib.ATTN_E_HEADDIM
+    assert _bwdv(causal=0, window=3) == _lib.ATTN_E_MASK
+    assert _bwdv(Hq=70000, Hkv=1) == _lib.ATTN_E_SHAPE
+    assert _bwdv(ws=None) == _lib.ATTN_E_WORKSPACE
+    assert _bwdv(ws_bytes=16) == _lib.ATTN_E_WORKSPACE
+    assert _bwdv(ptr=None, n=0) == _lib.ATTN_OK
