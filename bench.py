@@ -29,6 +29,17 @@ seeded dO) is timed after the steps, on its own, and reported under
 `backward` (TFLOP/s counting 2.5x the forward's flops, against the bf16 MFMA
 peak); it is not part of the step.  --skip-backward leaves it out.
 
+The packed-sequence forward (attn_fwd_varlen on 65536 tokens of sequences
+averaging about 600 tokens, at most 2048, 32 heads of 128, causal per
+sequence) is timed the same way and reported under `varlen`, with the
+fraction of a padded batch's work that would be useful (each sequence padded
+to 2048), and its backward (attn_bwd_varlen, 2.5x the forward's flops).
+--skip-varlen leaves both out.
+
+Chunked prefill over the paged cache (attn_prefill_paged: the decode batch's
+16 sequences of 8000..32000 cached tokens, each taking 512 new tokens) is
+reported under `prefill_paged` the same way; --skip-prefill-paged leaves it out.
+
 Other workloads can be timed with --workload NAME (one of the dense configs);
 the default line is the one described above.
 """
@@ -47,6 +58,8 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak; paged decode HBM GB/s + % peak"
 PREFILL = "mha_causal_8k"
 DECODE = "paged_decode_16x32k"
+PACKED = "packed_causal_64k_mean600"
+PREFILL_PAGED = "paged_prefill_16x32k_chunk512"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -80,6 +93,8 @@ def parse():
                     help="time only this dense workload's forward (extra lines)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
+    ap.add_argument("--skip-varlen", action="store_true")
+    ap.add_argument("--skip-prefill-paged", action="store_true")
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: a plain device copy of known size (counter calibration)")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
@@ -133,7 +148,8 @@ def write_traffic(src_dir):
     f_write = COPY_BYTES / (cwrite * 1024.0)
     out = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cfetch, "write_kib": cwrite,
                            "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)}}
-    groups = {f"fwd:{PREFILL}": (["fwd_bf16_kernel"], FWD_FILES),
+    # the dense forward: fwd_bf16_kernel<head dim, scale > 0, dense mode>
+    groups = {f"fwd:{PREFILL}": (["fwd_bf16_kernel<128, true, 0>"], FWD_FILES),
               f"decode:{DECODE}": (["decode_split_kernel", "decode_combine_kernel"],
                                    DECODE_FILES)}
     for key, (kernels, files) in groups.items():
@@ -332,6 +348,75 @@ def main():
                            "roofline": {"bound": "mfma", "achieved": round(btf, 2),
                                         "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                         "frac": round(btf / metrics.PEAK_BF16_TFLOPS, 4)}}
+    if not args.skip_varlen and args.workload is None:
+        print(f"bench: varlen {PACKED}", file=sys.stderr, flush=True)
+        from exact_softmax_attention_amd import attn_fwd_varlen
+        vc = workloads.PACKED_CONFIGS[PACKED]
+        pq, pk, pv, cu_q, cu_k = [t.to(dev) for t in workloads.make_packed_config(vc)]
+        pout = torch.empty_like(pq)
+        plse = torch.empty((vc.Hq, vc.total), dtype=torch.float32, device=dev)
+
+        def varlen():
+            attn_fwd_varlen(pq, pk, pv, cu_q, cu_k, causal=vc.causal, window=vc.window,
+                            scale=vc.scale, out=pout, lse=plse)
+
+        vper, _ = time_loop([varlen], max(2, args.steps), max(1, args.warmup), torch)
+        # its backward (attn_bwd_varlen) on a seeded dO
+        from exact_softmax_attention_amd import attn_bwd_varlen, attn_bwd_workspace_size
+        pdo = workloads.make_dout(1, vc.total, vc.Hq, vc.d, vc.seed)[0].to(dev)
+        pdq, pdk, pdv = torch.empty_like(pq), torch.empty_like(pk), torch.empty_like(pv)
+        pws = torch.empty(max(1, attn_bwd_workspace_size(1, vc.Hq, vc.total)), dtype=torch.uint8,
+                          device=dev)
+        varlen()
+
+        def varlen_bwd():
+            attn_bwd_varlen(pq, pk, pv, pout, pdo, plse, cu_q, cu_k, causal=vc.causal,
+                            window=vc.window, scale=vc.scale, dq=pdq, dk=pdk, dv=pdv,
+                            workspace=pws)
+
+        vbper, _ = time_loop([varlen_bwd], max(2, args.steps // 2), max(1, args.warmup), torch)
+        lens = (cu_q[1:] - cu_q[:-1]).cpu().numpy()
+        vflops = metrics.varlen_fwd_flops(lens, lens, vc.Hq, vc.d, vc.causal, vc.window)
+        padded = metrics.fwd_flops(len(lens), vc.Hq, vc.max_len, vc.max_len, vc.d, vc.causal,
+                                   vc.window)
+        vtf = vflops / (vper[0] * 1e-3) / 1e12
+        res["varlen"] = {"value": round(vtf, 2), "unit": "TFLOP/s", "ms": round(vper[0], 4),
+                         "workload": vc.name, "num_seqs": int(len(lens)),
+                         "mean_len": round(float(lens.mean()), 1), "max_len": int(lens.max()),
+                         "flop_per_call": vflops,
+                         "useful_fraction_if_padded": round(vflops / padded, 4),
+                         "kernel": "fwd_bf16_kernel<128, varlen>",
+                         "backward": {"value": round(2.5 * vflops / (vbper[0] * 1e-3) / 1e12, 2),
+                                      "unit": "TFLOP/s", "ms": round(vbper[0], 4),
+                                      "flop_per_call": 2.5 * vflops},
+                         "roofline": {"bound": "mfma", "achieved": round(vtf, 2),
+                                      "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(vtf / metrics.PEAK_BF16_TFLOPS, 4)}}
+    if not args.skip_prefill_paged and args.workload is None:
+        print(f"bench: prefill over the paged cache {PREFILL_PAGED}", file=sys.stderr, flush=True)
+        from exact_softmax_attention_amd import attn_prefill_paged
+        ppc = workloads.PREFILL_PAGED_CONFIGS[PREFILL_PAGED]
+        pin = {kk: t.to(dev) for kk, t in workloads.make_prefill_paged_config(ppc).items()}
+        ppout = torch.empty_like(pin["q"])
+        pplse = torch.empty((ppc.Hq, pin["q"].shape[0]), dtype=torch.float32, device=dev)
+
+        def prefill_paged():
+            attn_prefill_paged(pin["q"], pin["kcache"], pin["vcache"], pin["block_table"],
+                               pin["seq_lens"], pin["cu_seqlens_q"], scale=ppc.scale,
+                               window=ppc.window, out=ppout, lse=pplse)
+
+        pper, _ = time_loop([prefill_paged], max(2, args.steps), max(1, args.warmup), torch)
+        plens = pin["seq_lens"].cpu().numpy()
+        pch = (pin["cu_seqlens_q"][1:] - pin["cu_seqlens_q"][:-1]).cpu().numpy()
+        pflops = metrics.prefill_paged_flops(plens, pch, ppc.Hq, ppc.d, ppc.window)
+        ptf = pflops / (pper[0] * 1e-3) / 1e12
+        res["prefill_paged"] = {"value": round(ptf, 2), "unit": "TFLOP/s", "ms": round(pper[0], 4),
+                                "workload": ppc.name, "new_tokens": int(pch.sum()),
+                                "cached_tokens": int(plens.sum()), "flop_per_call": pflops,
+                                "kernel": "fwd_bf16_kernel<128, paged>",
+                                "roofline": {"bound": "mfma", "achieved": round(ptf, 2),
+                                             "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                             "frac": round(ptf / metrics.PEAK_BF16_TFLOPS, 4)}}
     if not args.skip_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(q, k, v, cfg)
