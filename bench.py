@@ -399,11 +399,15 @@ def main():
         pin = {kk: t.to(dev) for kk, t in workloads.make_prefill_paged_config(ppc).items()}
         ppout = torch.empty_like(pin["q"])
         pplse = torch.empty((ppc.Hq, pin["q"].shape[0]), dtype=torch.float32, device=dev)
+        from exact_softmax_attention_amd import attn_prefill_paged_workspace_size
+        ppws = torch.empty(max(1, attn_prefill_paged_workspace_size(
+            ppc.B, pin["q"].shape[0], ppc.Hq, ppc.d, ppc.block_size, ppc.max_blocks_per_seq)),
+            dtype=torch.uint8, device=dev)
 
         def prefill_paged():
             attn_prefill_paged(pin["q"], pin["kcache"], pin["vcache"], pin["block_table"],
                                pin["seq_lens"], pin["cu_seqlens_q"], scale=ppc.scale,
-                               window=ppc.window, out=ppout, lse=pplse)
+                               window=ppc.window, out=ppout, lse=pplse, workspace=ppws)
 
         pper, _ = time_loop([prefill_paged], max(2, args.steps), max(1, args.warmup), torch)
         plens = pin["seq_lens"].cpu().numpy()
@@ -413,7 +417,8 @@ def main():
         res["prefill_paged"] = {"value": round(ptf, 2), "unit": "TFLOP/s", "ms": round(pper[0], 4),
                                 "workload": ppc.name, "new_tokens": int(pch.sum()),
                                 "cached_tokens": int(plens.sum()), "flop_per_call": pflops,
-                                "kernel": "fwd_bf16_kernel<128, paged>",
+                                "kernels": "fwd_bf16_kernel<128, paged> + prefill_merge_kernel<128>",
+                                "workspace_bytes": int(ppws.numel()),
                                 "roofline": {"bound": "mfma", "achieved": round(ptf, 2),
                                              "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                              "frac": round(ptf / metrics.PEAK_BF16_TFLOPS, 4)}}

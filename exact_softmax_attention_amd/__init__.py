@@ -37,6 +37,7 @@ __all__ = [
     "attn_decode_paged",
     "attn_decode_paged_workspace_size",
     "attn_prefill_paged",
+    "attn_prefill_paged_workspace_size",
     "attn_bwd",
     "attn_bwd_workspace_size",
     "attn_bwd_varlen",
@@ -222,8 +223,15 @@ def attn_decode_paged(q, kcache, vcache, block_table, seq_lens, scale=None, wind
     return out, lse
 
 
+def attn_prefill_paged_workspace_size(num_seqs: int, total_q: int, Hq: int, d: int,
+                                      block_size: int, max_blocks_per_seq: int) -> int:
+    return int(_lib.lib().attn_prefill_paged_workspace_size(num_seqs, total_q, Hq, d, block_size,
+                                                            max_blocks_per_seq))
+
+
 def attn_prefill_paged(q, kcache, vcache, block_table, seq_lens, cu_seqlens_q, scale=None,
-                       window: int = 0, out=None, lse=None, return_lse: bool = True):
+                       window: int = 0, out=None, lse=None, return_lse: bool = True,
+                       workspace=None):
     """Chunked prefill over a paged cache (always causal).  Returns (out, lse).
 
     Sequence s owns rows cu_seqlens_q[s]:cu_seqlens_q[s+1] of q/out: its new
@@ -259,11 +267,17 @@ def attn_prefill_paged(q, kcache, vcache, block_table, seq_lens, cu_seqlens_q, s
         _dev(lse, "lse", torch.float32)
         if lse.shape != (Hq, total_q):
             raise ValueError("lse must be [Hq, total_q]")
+    need = attn_prefill_paged_workspace_size(S, total_q, Hq, d, block_size, block_table.shape[1])
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device.type != "cuda":
+        raise ValueError("workspace must be on the GPU")
     code = _lib.lib().attn_prefill_paged(
         q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), block_table.data_ptr(),
         seq_lens.data_ptr(), cu_seqlens_q.data_ptr(), out.data_ptr(),
         lse.data_ptr() if lse is not None else None, S, total_q, Hq, Hkv, d, block_size,
-        block_table.shape[1], num_blocks, int(window), float(scale), _stream(q.device))
+        block_table.shape[1], num_blocks, int(window), float(scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "attn_prefill_paged")
     return out, lse
 

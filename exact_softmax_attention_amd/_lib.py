@@ -31,8 +31,9 @@ SIGNATURES = {
     "attn_decode_paged_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                _P, _SZ, _P]),
+    "attn_prefill_paged_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "attn_prefill_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
-                                _I, _F, _P]),
+                                _I, _F, _P, _SZ, _P]),
     "attn_bwd_workspace_size": (_SZ, [_I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                       _P, _SZ, _P]),

@@ -108,26 +108,38 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+size_t attn_prefill_paged_workspace_size(int num_seqs, int total_q, int Hq, int d, int block_size,
+                                         int max_blocks_per_seq) {
+  if (num_seqs < 0 || total_q < 0 || Hq < 1 || (d != 64 && d != 128) || block_size != 16 ||
+      max_blocks_per_seq < 1 || (long long)max_blocks_per_seq * block_size > INT_MAX)
+    return 0;
+  return attn::prefill_paged_workspace_bytes(num_seqs, Hq, total_q, d, max_blocks_per_seq);
+}
+
 int attn_prefill_paged(const void* q, const void* kcache, const void* vcache,
                        const int* block_table, const int* seq_lens, const int* cu_seqlens_q,
                        void* out, float* lse, int num_seqs, int total_q, int Hq, int Hkv, int d,
                        int block_size, int max_blocks_per_seq, int num_blocks, int window,
-                       float scale, void* stream) {
+                       float scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || total_q < 0) return ATTN_E_SHAPE;
   const int st = check_common(num_seqs, Hq, Hkv, d);
   if (st != ATTN_OK) return st;
   if (block_size != 16 || max_blocks_per_seq < 1 || num_blocks < 1) return ATTN_E_SHAPE;
   if ((long long)max_blocks_per_seq * block_size > INT_MAX) return ATTN_E_SHAPE;
   if ((long long)num_seqs * max_blocks_per_seq > INT_MAX) return ATTN_E_SHAPE;
-  if (attn::fwd_bf16_varlen_grid(num_seqs, Hq, total_q) > INT_MAX) return ATTN_E_SHAPE;
+  if (attn::prefill_paged_grid(num_seqs, Hq, total_q, max_blocks_per_seq) > INT_MAX)
+    return ATTN_E_SHAPE;
   if ((long long)Hkv * d > (1LL << 22)) return ATTN_E_SHAPE;
   if (num_seqs == 0 || total_q == 0) return ATTN_OK;
   if (!q || !out || !kcache || !vcache || !block_table || !seq_lens || !cu_seqlens_q)
     return ATTN_E_NULL;
+  const size_t need =
+      attn::prefill_paged_workspace_bytes(num_seqs, Hq, total_q, d, max_blocks_per_seq);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_E_WORKSPACE;
   attn::PrefillPagedArgs a{q,           kcache,   vcache,          block_table, seq_lens,
                            cu_seqlens_q, out,     lse,             num_seqs,    total_q,
                            Hq,           Hkv,     d,               max_blocks_per_seq,
-                           num_blocks,   window > 0 ? window : 0,  scale};
+                           num_blocks,   window > 0 ? window : 0,  scale,       workspace};
   const hipError_t e = attn::launch_prefill_paged(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }

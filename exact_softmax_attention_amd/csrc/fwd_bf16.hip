@@ -108,12 +108,37 @@ struct Params {
   const int* table;
   const int* seq_lens;
   int max_blocks, num_blocks;
+  // paged: an item whose key tiles span several chunks of chunk_tiles tiles
+  // is done as one work unit per chunk, each writing its normalised partial
+  // O (fp32) and LSE to part_o [Hq][vtiles][chunks][kBM][D] and part_lse
+  // [Hq][vtiles][chunks][kBM]; a merge kernel combines them
+  int chunks, chunk_tiles;
+  float* part_o;
+  float* part_lse;
 };
 
 // What the kernel reads: dense [B, N, H, D] tensors, packed sequences
 // (cu_seqlens), or packed query chunks over a paged KV cache.
 enum Mode { kDense = 0, kVarlen = 1, kPaged = 2 };
 constexpr int kBlockTokens = 16;  // tokens per cache block
+constexpr int kChunkTiles = 128;  // paged: 64-key tiles per key chunk (8192 keys)
+
+// Key tiles (64 keys) that query rows [i0, i0 + kBM) of a sequence with Nq
+// queries and Nk keys may see: [t_begin, t_begin + n_tiles).
+struct TileRange {
+  int t_begin, n_tiles;
+};
+__device__ __forceinline__ TileRange tile_range(int i0, int Nq, int Nk, int causal, int window) {
+  const int delta = Nk - Nq;
+  int kv_end = Nk;
+  if (causal) kv_end = min(Nk, i0 + kBM + delta);
+  int kv_begin = 0;
+  if (window > 0) kv_begin = max(0, i0 + delta - window + 1);
+  TileRange r;
+  r.t_begin = kv_begin / 64;
+  r.n_tiles = kv_end > kv_begin ? (kv_end + 63) / 64 - r.t_begin : 0;
+  return r;
+}
 
 // Scheduling counters of the persistent kernel: slot s holds one item counter
 // per XCD and a count of finished work groups.  Launches take slots in turn,
@@ -276,13 +301,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     int b, h, qt, Nq, Nk;
     int64_t q_tok0, k_tok0, lse0;
     bool bad = false;  // paged: a length or block id the kernel cannot read
+    int slot = 0, chunk = 0;  // packed: schedule slot; paged: key chunk
     if constexpr (VARLEN) {
       // unit = (KV head, tile slot, query head within the group); the slots
       // of sequence s start at cu_q[s] / kBM + s, which leaves room for its
       // tiles (heaviest first), and a slot past them is skipped
       const int hg = unit % p.group;
-      const int rest = unit / p.group;
-      const int slot = rest % p.vtiles;
+      int rest = unit / p.group;
+      if constexpr (PAGED) {  // the chunks of one item are neighbours in the queue
+        chunk = rest % p.chunks;
+        rest /= p.chunks;
+      }
+      slot = rest % p.vtiles;
       h = (rest / p.vtiles) * p.group + hg;
       b = find_seq<kBM>(p.cu_q, p.n_seqs, p.total_q, slot, lane);
       const int q0 = clampi(p.cu_q[b], 0, p.total_q);
@@ -325,12 +355,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     const int qw0 = i0 + wave * kRowsPerWave;
     const int delta = Nk - Nq;
 
-    int kv_end = Nk;
-    if (p.causal) kv_end = min(Nk, i0 + kBM + delta);
-    int kv_begin = 0;
-    if (p.window > 0) kv_begin = max(0, i0 + delta - p.window + 1);
-    const int t_begin = kv_begin / T::BN;
-    const int n_tiles = kv_end > kv_begin ? (kv_end + T::BN - 1) / T::BN - t_begin : 0;
+    static_assert(T::BN == 64, "tile_range counts 64-key tiles");
+    const TileRange tr_ = tile_range(i0, Nq, Nk, p.causal, p.window);
+    int t_begin = tr_.t_begin;
+    int n_tiles = tr_.n_tiles;
+    bool split = false;  // paged: this unit does one chunk of the item's tiles
+    if constexpr (PAGED) {
+      const int c0 = n_tiles > 0 ? t_begin / p.chunk_tiles : 0;
+      const int c1 = n_tiles > 0 ? (t_begin + n_tiles - 1) / p.chunk_tiles : 0;
+      if (chunk < c0 || chunk > c1) {
+        __syncthreads();  // as for a skipped slot: s_unit is read before it is rewritten
+        break;
+      }
+      split = c1 > c0;
+      if (split) {
+        const int lo = max(t_begin, chunk * p.chunk_tiles);
+        const int hi = min(t_begin + n_tiles, (chunk + 1) * p.chunk_tiles);
+        t_begin = lo;
+        n_tiles = hi - lo;
+      }
+    }
 
     // this wave's Q rows as the B operand of K Q^T (8 bf16 per k-chunk)
     const int64_t q_row = (int64_t)p.Hq * D;
@@ -382,7 +426,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     // item bad and is not read.
     static_assert(T::LPW * 1024 / T::ROWB == 8, "8 rows per wave and tile");
     constexpr int kNone = INT_MIN;
-    const int* const trow = PAGED ? p.table + (int64_t)b * p.max_blocks : nullptr;
+    // read through the constant address space: the index is uniform, so these
+    // become scalar loads (lgkmcnt), which do not wait behind the vector
+    // memory counter that paces the tile loads
+    typedef const __attribute__((address_space(4))) int const_int;
+    const_int* const trow = (const_int*)(PAGED ? p.table + (int64_t)b * p.max_blocks : p.table);
     const int64_t blk_b = (int64_t)kBlockTokens * kv_row * 2;  // bytes per cache block
     auto lookup = [&](int t) __attribute__((always_inline)) {
       const int lb = (t_begin + t) * (T::BN / kBlockTokens) + (wave >> 1);
@@ -750,6 +798,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     const float l_tot = la + lb;
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (PAGED && bad) inv = __builtin_nanf("");  // O and LSE of the whole item are NaN
+    if (PAGED && split) {
+      // this chunk's normalised O in fp32 and its LSE, for the merge kernel
+      const int row = qw0 + n;  // row of the sequence; row - i0 is its row in the tile
+      const int64_t prow = ((int64_t)(h * p.vtiles + slot) * p.chunks + chunk) * kBM + (row - i0);
+      if (row < Nq) {
+  #pragma unroll
+        for (int db = 0; db < T::NDB; ++db)
+  #pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            f32x4 w;
+            w[0] = acc[db][r4 * 4 + 0] * inv;
+            w[1] = acc[db][r4 * 4 + 1] * inv;
+            w[2] = acc[db][r4 * 4 + 2] * inv;
+            w[3] = acc[db][r4 * 4 + 3] * inv;
+            *reinterpret_cast<f32x4*>(p.part_o + prow * D + db * 32 + r4 * 8 + g * 4) = w;
+          }
+        if (g == 0)
+          p.part_lse[prow] = bad ? __builtin_nanf("")
+                             : l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+      }
+    } else {
     constexpr int OPITCH = T::ROWB + 16;  // bytes per staged row
     static_assert(kWaves * kRowsPerWave * OPITCH <= T::LDS_BYTES, "O staging fits the ring");
     const uint32_t ostage = wave * kRowsPerWave * OPITCH;
@@ -780,6 +849,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     if (row < Nq && p.lse != nullptr && g == 0)
       p.lse[lse0 + row] = (PAGED && bad) ? __builtin_nanf("")
                           : l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
   }
   // the O staging is done with the ring before the next unit's loads
   if (tid == 0) s_unit = first + grabbed;
@@ -794,6 +864,67 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     if (atomicAdd(ctr + kXcd, 1) == G - 1) {
       for (int x = 0; x <= kXcd; ++x) atomicExch(ctr + x, 0);
     }
+  }
+}
+
+// Paged chunked prefill, second pass: rows of items done in several key
+// chunks merge the chunks' (O_c, LSE_c): M = max LSE_c, w_c = exp(LSE_c - M),
+// O = sum w_c O_c / sum w_c, LSE = M + ln sum w_c (the exact merge of partial
+// softmax states).  One work group per (schedule slot, query head); a wave
+// per row at a time, the lanes along the features.  A NaN partial (a block
+// the first pass could not read) gives NaN.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const Params p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slot = blockIdx.x, h = blockIdx.y;
+  const int b = find_seq<kBM>(p.cu_q, p.n_seqs, p.total_q, slot, lane);
+  const int q0 = clampi(p.cu_q[b], 0, p.total_q);
+  const int Nq = clampi(p.cu_q[b + 1], q0, p.total_q) - q0;
+  const int len = p.seq_lens[b];
+  if (len < 0 || len > p.max_blocks * kBlockTokens) return;  // written as NaN by the first pass
+  const int off = slot - (q0 / kBM + b);
+  const int ntl = (Nq + kBM - 1) / kBM;
+  if (off < 0 || off >= ntl) return;
+  const int qt = ntl - 1 - off;
+  const TileRange tr = tile_range(qt * kBM, Nq, len, 1, p.window);
+  if (tr.n_tiles == 0) return;
+  const int c0 = tr.t_begin / p.chunk_tiles;
+  const int c1 = (tr.t_begin + tr.n_tiles - 1) / p.chunk_tiles;
+  if (c1 == c0) return;  // written directly by the first pass
+  constexpr int F = D / 64;  // features per lane
+  const int64_t base = (int64_t)(h * p.vtiles + slot) * p.chunks * kBM;
+  const int64_t q_row = (int64_t)p.Hq * D;
+  for (int r = wave; r < kBM && qt * kBM + r < Nq; r += 4) {
+    float m = kNegInf;
+    bool nan = false;
+    for (int c = c0; c <= c1; ++c) {
+      const float l = p.part_lse[base + (int64_t)c * kBM + r];
+      nan |= l != l;
+      m = fmaxf(m, l);
+    }
+    float o[F] = {};
+    float sum = 0.f;
+    if (m != kNegInf) {
+      for (int c = c0; c <= c1; ++c) {
+        const int64_t pr = base + (int64_t)c * kBM + r;
+        const float w = fast_exp2((p.part_lse[pr] - m) * kLog2e);
+        sum += w;
+  #pragma unroll
+        for (int f = 0; f < F; ++f) o[f] += w * p.part_o[pr * D + lane * F + f];
+      }
+    }
+    const float inv = nan ? __builtin_nanf("") : sum > 0.f ? 1.f / sum : 0.f;
+    const int row = qt * kBM + r;
+    uint16_t* op = p.o + ((int64_t)q0 + row) * q_row + (int64_t)h * D + lane * F;
+    if constexpr (F == 2) {
+      *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(o[0] * inv, o[1] * inv);
+    } else {
+      *op = (uint16_t)(pack_bf16x2(o[0] * inv, 0.f) & 0xffffu);
+    }
+    if (lane == 0 && p.lse != nullptr)
+      p.lse[(int64_t)h * p.total_q + q0 + row] =
+          nan ? __builtin_nanf("") : sum > 0.f ? m + fast_log2(sum) * kLn2 : kNegInf;
   }
 }
 
@@ -907,9 +1038,47 @@ hipError_t launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream) {
   p.vtiles = a.total_q / kBM + a.n_seqs;
   p.n_qtiles = 1;
   p.pairing = 0;
-  p.total = (int)fwd_bf16_varlen_grid(a.n_seqs, a.Hq, a.total_q);
+  p.chunk_tiles = kChunkTiles;
+  p.chunks = prefill_paged_chunks(a.max_blocks_per_seq);
+  char* ws = static_cast<char*>(a.workspace);
+  p.part_o = reinterpret_cast<float*>(ws);
+  p.part_lse = reinterpret_cast<float*>(
+      ws + prefill_paged_part_o_bytes(a.n_seqs, a.Hq, a.total_q, a.d, a.max_blocks_per_seq));
+  p.total = (int)prefill_paged_grid(a.n_seqs, a.Hq, a.total_q, a.max_blocks_per_seq);
   if (a.n_seqs == 0 || a.total_q == 0) return hipSuccess;
-  return launch<kPaged>(p, a.d, a.scale, p.total, stream);
+  const hipError_t e = launch<kPaged>(p, a.d, a.scale, p.total, stream);
+  if (e != hipSuccess || p.chunks == 1) return e;
+  const dim3 grid(p.vtiles, a.Hq);
+  if (a.d == 128)
+    hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(prefill_merge_kernel<64>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+int prefill_paged_chunks(int max_blocks_per_seq) {
+  const long long tiles = ((long long)max_blocks_per_seq * kBlockTokens + 63) / 64;
+  return (int)((tiles + kChunkTiles - 1) / kChunkTiles);
+}
+
+long long prefill_paged_grid(int n_seqs, int Hq, int total_q, int max_blocks_per_seq) {
+  return fwd_bf16_varlen_grid(n_seqs, Hq, total_q) * prefill_paged_chunks(max_blocks_per_seq);
+}
+
+size_t prefill_paged_part_o_bytes(int n_seqs, int Hq, int total_q, int d, int max_blocks_per_seq) {
+  const int c = prefill_paged_chunks(max_blocks_per_seq);
+  if (c <= 1) return 0;
+  const size_t rows = (size_t)fwd_bf16_varlen_grid(n_seqs, Hq, total_q) * c * kBM;
+  return (rows * d * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t prefill_paged_workspace_bytes(int n_seqs, int Hq, int total_q, int d,
+                                     int max_blocks_per_seq) {
+  const int c = prefill_paged_chunks(max_blocks_per_seq);
+  if (c <= 1) return 0;
+  const size_t rows = (size_t)fwd_bf16_varlen_grid(n_seqs, Hq, total_q) * c * kBM;
+  return prefill_paged_part_o_bytes(n_seqs, Hq, total_q, d, max_blocks_per_seq) +
+         (rows * sizeof(float) + 255) / 256 * 256;
 }
 
 }  // namespace attn

@@ -61,9 +61,17 @@ struct PrefillPagedArgs {
   float* lse;
   int n_seqs, total_q, Hq, Hkv, d, max_blocks_per_seq, num_blocks, window;
   float scale;
+  void* workspace;  // prefill_paged_workspace_bytes(...) bytes (none when 0)
 };
 
 hipError_t launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream);
+// Key chunks an item may be split into, work units, and the partial-result
+// workspace (fp32 O then LSE per chunk and row; 0 bytes when nothing splits).
+int prefill_paged_chunks(int max_blocks_per_seq);
+long long prefill_paged_grid(int n_seqs, int Hq, int total_q, int max_blocks_per_seq);
+size_t prefill_paged_part_o_bytes(int n_seqs, int Hq, int total_q, int d, int max_blocks_per_seq);
+size_t prefill_paged_workspace_bytes(int n_seqs, int Hq, int total_q, int d,
+                                     int max_blocks_per_seq);
 
 struct DecodeArgs {
   const void* q;

@@ -184,12 +184,24 @@ int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace attn_prefill_paged needs for these sizes (0 when
+ * no query tile can need more than one key chunk of 8192 keys, i.e.
+ * max_blocks_per_seq * block_size <= 8192; 0 for invalid sizes).  Pure host
+ * function; no HIP call.
+ */
+size_t attn_prefill_paged_workspace_size(int num_seqs, int total_q, int Hq, int d,
+                                         int block_size, int max_blocks_per_seq);
+
+/*
  * Chunked prefill over a block-paged KV cache ("Ch. 3: MHA Limitations, MQA,
  * GQA, and FlashAttention": 3.1, new tokens attend to the cache after their
  * own K/V are appended; the GQA code of 3.3 notes that a cache needs its own
  * causal handling; "Inference Engineering", 2.5: the cache is split into
  * blocks reached through a lookup table).  The kernel of attn_fwd reading
- * K/V through the table.
+ * K/V through the table.  A 256-row query tile whose keys span more than one
+ * 8192-key chunk is computed chunk by chunk (separate work units, partial
+ * results in the workspace) and merged by a second kernel on the same stream
+ * ("Ch. 3" 3.5: partial softmax states merge exactly).
  *
  *   q, out        [total_q, Hq, d] bf16: each sequence's new tokens back to back
  *   cu_seqlens_q  [num_seqs + 1] int32 (device): sequence s owns rows
@@ -200,6 +212,10 @@ int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
  *   seq_lens      [num_seqs] int32 (device): cached tokens of sequence s, its
  *                 new tokens included (they are the last nq_s of them)
  *   lse           [Hq, total_q] float32, or NULL
+ *   workspace     attn_prefill_paged_workspace_size(...) bytes of device
+ *                 memory owned by the caller (may be NULL when that is 0); its
+ *                 contents on entry do not matter; calls that share it must
+ *                 not overlap
  *
  * Always causal: new row i of sequence s sits at position seq_lens[s] - nq_s
  * + i and sees the cached tokens up to it (the last `window` of them when
@@ -213,14 +229,15 @@ int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
  * array follows the rules of attn_fwd_varlen.
  *
  * block_size must be 16; d in {64, 128}; Hq % Hkv == 0; num_seqs *
- * max_blocks_per_seq <= INT_MAX; Hq * (total_q / 256 + num_seqs) <= INT_MAX
- * (ATTN_E_SHAPE otherwise).
+ * max_blocks_per_seq <= INT_MAX; Hq * (total_q / 256 + num_seqs) * chunks <=
+ * INT_MAX with chunks = ceil(max_blocks_per_seq * 16 / 8192) (ATTN_E_SHAPE
+ * otherwise); ATTN_E_WORKSPACE for a missing or short workspace.
  */
 int attn_prefill_paged(const void* q, const void* kcache, const void* vcache,
                        const int* block_table, const int* seq_lens, const int* cu_seqlens_q,
                        void* out, float* lse, int num_seqs, int total_q, int Hq, int Hkv, int d,
                        int block_size, int max_blocks_per_seq, int num_blocks, int window,
-                       float scale, void* stream);
+                       float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace attn_bwd needs (two float32 values per query row

@@ -151,9 +151,10 @@ def test_varlen_validation():
     assert _varlen(ptr=None, cu=None, tq=0) == _lib.ATTN_OK
 
 
-def _prefill(ptr=1 << 20, n=3, tq=100, Hq=8, Hkv=2, d=128, bs=16, mb=8, nb=40, window=0):
+def _prefill(ptr=1 << 20, n=3, tq=100, Hq=8, Hkv=2, d=128, bs=16, mb=8, nb=40, window=0,
+             ws=None, ws_bytes=0):
     return _lib.lib().attn_prefill_paged(ptr, ptr, ptr, ptr, ptr, ptr, ptr, None, n, tq, Hq,
-                                         Hkv, d, bs, mb, nb, window, 0.1, None)
+                                         Hkv, d, bs, mb, nb, window, 0.1, ws, ws_bytes, None)
 
 
 def test_prefill_paged_validation():
@@ -167,6 +168,21 @@ def test_prefill_paged_validation():
     assert _prefill(n=1 << 20, mb=1 << 12) == _lib.ATTN_E_SHAPE   # table entries
     assert _prefill(ptr=None, n=0) == _lib.ATTN_OK
     assert _prefill(ptr=None, tq=0) == _lib.ATTN_OK
+    # a table longer than one 8192-key chunk needs the partial-result workspace
+    assert _prefill(mb=600) == _lib.ATTN_E_WORKSPACE
+    need = _lib.lib().attn_prefill_paged_workspace_size(3, 100, 8, 128, 16, 600)
+    assert _prefill(mb=600, ws=1 << 20, ws_bytes=need - 1) == _lib.ATTN_E_WORKSPACE
+
+
+def test_prefill_paged_workspace_size():
+    ws = _lib.lib().attn_prefill_paged_workspace_size
+    assert ws(3, 100, 8, 128, 16, 512) == 0          # 8192 keys: one chunk, no partials
+    slots, chunks = 100 // 256 + 3, 2                  # 513 blocks: two chunks
+    rows = 8 * slots * chunks * 256
+    align = lambda x: (x + 255) // 256 * 256
+    assert ws(3, 100, 8, 128, 16, 513) == align(rows * 128 * 4) + align(rows * 4)
+    assert ws(3, 100, 8, 128, 32, 513) == 0           # bad block size
+    assert ws(-1, 100, 8, 128, 16, 513) == 0
 
 
 def _bwdv(ptr=1 << 20, n=2, tq=300, tk=300, Hq=4, Hkv=2, d=128, causal=1, window=0, ws=1 << 22,

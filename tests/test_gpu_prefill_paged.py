@@ -70,6 +70,26 @@ def test_small_chunks(case):
     check(out, O, lse, L, "bf16", _ids(case))
 
 
+SPLIT = [
+    # contexts past one 8192-key chunk: query tiles whose keys span 2..3 chunks
+    ([9000, 300, 20000], [100, 300, 257], 4, 2, 128, 0),
+    ([16385, 8193], [600, 1], 2, 1, 64, 0),
+    ([20000, 12000], [300, 260], 4, 4, 128, 9000),  # windows across a chunk boundary
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=_ids)
+def test_key_chunk_split(case):
+    lens, chunks, Hq, Hkv, d, window = case
+    seed = 3050 + SPLIT.index(case)
+    print(f"case {_ids(case)} seed {seed}", flush=True)
+    inp = _make(lens, chunks, Hq, Hkv, d, seed)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    out, lse = _run(inp, scale, window)
+    O, L = _oracle(inp, scale, window)
+    check(out, O, lse, L, "bf16", _ids(case))
+
+
 def test_one_new_token_matches_decode():
     lens = [40, 700, 1234, 16]
     inp = _make(lens, [1] * 4, 8, 2, 128, 3100)
