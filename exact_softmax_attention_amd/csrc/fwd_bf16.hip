@@ -893,38 +893,77 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const Params p) {
   const int c1 = (tr.t_begin + tr.n_tiles - 1) / p.chunk_tiles;
   if (c1 == c0) return;  // written directly by the first pass
   constexpr int F = D / 64;  // features per lane
+  constexpr int R = 4;       // rows of a wave in flight together
+  constexpr int CG = 4;      // chunks whose loads are issued together
   const int64_t base = (int64_t)(h * p.vtiles + slot) * p.chunks * kBM;
   const int64_t q_row = (int64_t)p.Hq * D;
-  for (int r = wave; r < kBM && qt * kBM + r < Nq; r += 4) {
-    float m = kNegInf;
-    bool nan = false;
-    for (int c = c0; c <= c1; ++c) {
-      const float l = p.part_lse[base + (int64_t)c * kBM + r];
-      nan |= l != l;
-      m = fmaxf(m, l);
-    }
-    float o[F] = {};
-    float sum = 0.f;
-    if (m != kNegInf) {
-      for (int c = c0; c <= c1; ++c) {
-        const int64_t pr = base + (int64_t)c * kBM + r;
-        const float w = fast_exp2((p.part_lse[pr] - m) * kLog2e);
-        sum += w;
+  const int nrows = min(kBM, Nq - qt * kBM);
+  for (int r0 = wave * R; r0 < nrows; r0 += 4 * R) {
+    // pass 1: the largest LSE of each row (NaN noted separately: fmaxf drops it)
+    float m[R];
+    bool nan[R];
   #pragma unroll
-        for (int f = 0; f < F; ++f) o[f] += w * p.part_o[pr * D + lane * F + f];
+    for (int i = 0; i < R; ++i) {
+      m[i] = kNegInf;
+      nan[i] = false;
+    }
+    for (int cb = c0; cb <= c1; cb += CG) {
+      float l[R][CG];
+  #pragma unroll
+      for (int i = 0; i < R; ++i)
+  #pragma unroll
+        for (int j = 0; j < CG; ++j)
+          l[i][j] = (cb + j <= c1 && r0 + i < nrows)
+                        ? p.part_lse[base + (int64_t)(cb + j) * kBM + r0 + i] : kNegInf;
+  #pragma unroll
+      for (int i = 0; i < R; ++i)
+  #pragma unroll
+        for (int j = 0; j < CG; ++j) {
+          nan[i] |= l[i][j] != l[i][j];
+          m[i] = fmaxf(m[i], l[i][j]);
+        }
+    }
+    // pass 2: weights and the weighted sum of the chunks' O
+    float o[R][F] = {};
+    float sum[R] = {};
+    for (int cb = c0; cb <= c1; cb += CG) {
+      float w[R][CG];
+      float v[R][CG][F];
+  #pragma unroll
+      for (int i = 0; i < R; ++i)
+  #pragma unroll
+        for (int j = 0; j < CG; ++j) {
+          const bool ok = cb + j <= c1 && r0 + i < nrows;
+          const int64_t pr = base + (int64_t)(cb + j) * kBM + r0 + i;
+          w[i][j] = ok ? p.part_lse[pr] : kNegInf;
+  #pragma unroll
+          for (int f = 0; f < F; ++f) v[i][j][f] = ok ? p.part_o[pr * D + lane * F + f] : 0.f;
+        }
+  #pragma unroll
+      for (int i = 0; i < R; ++i)
+  #pragma unroll
+        for (int j = 0; j < CG; ++j) {
+          const float wt = m[i] == kNegInf ? 0.f : fast_exp2((w[i][j] - m[i]) * kLog2e);
+          sum[i] += wt;
+  #pragma unroll
+          for (int f = 0; f < F; ++f) o[i][f] += wt * v[i][j][f];
+        }
+    }
+  #pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (r0 + i >= nrows) break;
+      const float inv = nan[i] ? __builtin_nanf("") : sum[i] > 0.f ? 1.f / sum[i] : 0.f;
+      const int row = qt * kBM + r0 + i;
+      uint16_t* op = p.o + ((int64_t)q0 + row) * q_row + (int64_t)h * D + lane * F;
+      if constexpr (F == 2) {
+        *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(o[i][0] * inv, o[i][1] * inv);
+      } else {
+        *op = (uint16_t)(pack_bf16x2(o[i][0] * inv, 0.f) & 0xffffu);
       }
+      if (lane == 0 && p.lse != nullptr)
+        p.lse[(int64_t)h * p.total_q + q0 + row] =
+            nan[i] ? __builtin_nanf("") : sum[i] > 0.f ? m[i] + fast_log2(sum[i]) * kLn2 : kNegInf;
     }
-    const float inv = nan ? __builtin_nanf("") : sum > 0.f ? 1.f / sum : 0.f;
-    const int row = qt * kBM + r;
-    uint16_t* op = p.o + ((int64_t)q0 + row) * q_row + (int64_t)h * D + lane * F;
-    if constexpr (F == 2) {
-      *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(o[0] * inv, o[1] * inv);
-    } else {
-      *op = (uint16_t)(pack_bf16x2(o[0] * inv, 0.f) & 0xffffu);
-    }
-    if (lane == 0 && p.lse != nullptr)
-      p.lse[(int64_t)h * p.total_q + q0 + row] =
-          nan ? __builtin_nanf("") : sum > 0.f ? m + fast_log2(sum) * kLn2 : kNegInf;
   }
 }
 
