@@ -36,6 +36,9 @@ fraction of a padded batch's work that would be useful (each sequence padded
 to 2048), and its backward (attn_bwd_varlen, 2.5x the forward's flops).
 --skip-varlen leaves both out.
 
+The fp32 single-head case (attn_fwd_f32, 1 x 256 x 1 x 64, non-causal) is
+timed in microseconds under `f32_single_head` (launch-latency bound).
+
 Chunked prefill over the paged cache (attn_prefill_paged: the decode batch's
 16 sequences of 8000..32000 cached tokens, each taking 512 new tokens) is
 reported under `prefill_paged` the same way; --skip-prefill-paged leaves it out.
@@ -422,6 +425,22 @@ def main():
                                 "roofline": {"bound": "mfma", "achieved": round(ptf, 2),
                                              "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                              "frac": round(ptf / metrics.PEAK_BF16_TFLOPS, 4)}}
+    if args.workload is None:
+        # the fp32 single-head case (1 x 256 x 1 x 64): launch-latency bound,
+        # reported in microseconds only
+        from exact_softmax_attention_amd import attn_fwd_f32
+        fc = workloads.DENSE_CONFIGS["f32_single_head_256"]
+        fq, fk, fv = [t.to(dev) for t in workloads.make_dense_config(fc)]
+        fout, flse = torch.empty_like(fq), torch.empty((1, 1, fc.Nq), device=dev)
+
+        def f32_fwd():
+            attn_fwd_f32(fq, fk, fv, causal=fc.causal, window=fc.window, scale=fc.scale,
+                         out=fout, lse=flse)
+
+        fper, _ = time_loop([f32_fwd], max(20, args.steps), max(3, args.warmup), torch)
+        res["f32_single_head"] = {"us": round(fper[0] * 1e3, 2), "workload": fc.name,
+                                  "kernel": "fwd_f32_kernel<64>",
+                                  "note": "launch-latency bound; no roofline fraction"}
     if not args.skip_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(q, k, v, cfg)

@@ -235,7 +235,10 @@ def attn_prefill_paged(q, kcache, vcache, block_table, seq_lens, cu_seqlens_q, s
     """Chunked prefill over a paged cache (always causal).  Returns (out, lse).
 
     Sequence s owns rows cu_seqlens_q[s]:cu_seqlens_q[s+1] of q/out: its new
-    tokens, the last of its seq_lens[s] cached tokens.
+    tokens, the last of its seq_lens[s] cached tokens.  ``workspace`` (uint8 on
+    the GPU, at least attn_prefill_paged_workspace_size(...) bytes) holds the
+    partial results of query tiles split along the keys; one is allocated per
+    call when it is not given.
     """
     _dev(q, "q", torch.bfloat16)
     _dev(kcache, "kcache", torch.bfloat16)
