@@ -44,6 +44,12 @@
 //   * Work groups are ordered heavy-first (last query tiles first) inside a
 //     head and remapped so that the tiles of one head share an XCD (and its
 //     L2), since they all stream the same K/V.
+//   * Three modes share the loop: dense [B, N, H, D] tensors; packed
+//     sequences of different lengths (cu_seqlens offsets; packed sequence
+//     boundaries are what "How to Reduce Attention Computation Cost in LLM
+//     Training" says need variable-length kernels); and new tokens over a
+//     block-paged KV cache ("Inference Engineering", 2.5), where each wave
+//     loads its 8 rows of a key tile from the cache block that holds them.
 #include <atomic>
 #include <climits>
 #include <type_traits>
@@ -269,7 +275,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   // (work group w runs on XCD w % 8); each XCD hands out its range through its
   // own counter.  So the groups of an XCD work on the same few heads at a time
   // (their K/V stream through the XCD's L2), and the cheap units, taken last,
-  // even out the finishing times whatever the cost of each unit.
+  // even out the finishing times whatever the cost of each unit.  Packed
+  // sequences and the paged cache (modes 1 and 2) have no pairing: a unit is
+  // one query tile of one head of one sequence (paged: and one key chunk),
+  // found from the unit index as described at the item setup below.
   constexpr int kXcd = kXcds;
   __shared__ int s_unit;  // the next unit, broadcast from thread 0
   __shared__ int s_bad;   // paged: some wave met a block it cannot read
