@@ -61,7 +61,10 @@
  *     visible keys, in float32.
  *   - `scale` is used as given (callers normally pass 1/sqrt(d)).
  *   - The library is thread-safe.  Its only state is a per-device cache of the
- *     compute-unit count, filled on first use.
+ *     compute-unit count, filled on first use, and the forward kernel's
+ *     scheduling counters in device memory: 64 slots that launches take in
+ *     turn, each returned to zero by the launch that used it, so up to 64
+ *     forward launches may be in flight at once (on any streams).
  */
 #ifndef ATTN_MI355X_ATTN_H
 #define ATTN_MI355X_ATTN_H
