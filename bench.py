@@ -43,6 +43,11 @@ Chunked prefill over the paged cache (attn_prefill_paged: the decode batch's
 16 sequences of 8000..32000 cached tokens, each taking 512 new tokens) is
 reported under `prefill_paged` the same way; --skip-prefill-paged leaves it out.
 
+With the CPU baseline on, the backward, packed and chunked-prefill objects
+carry their own `cpu_baseline`: the fp64 oracle timed on a bounded sample of
+that workload (one head, sixteen sequences, one sequence), scaled by the
+sample's flops.
+
 Other workloads can be timed with --workload NAME (one of the dense configs);
 the default line is the one described above.
 """
@@ -191,6 +196,21 @@ def cpu_baseline(q, k, v, cfg, n_heads=16):
                       f"{cfg.Nq} rows, fp64 NumPy materialising S and P; {dt:.2f} s, scaled by "
                       "causal-adjusted FLOPs",
             "seconds": round(dt, 3), "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_sample(fn, flops, sample):
+    """Time one call of an oracle function on a bounded sample; its flops -> TFLOP/s."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                        if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
 
 
 def time_loop(fns, steps, warmup, torch):
@@ -348,6 +368,13 @@ def main():
         res["backward"] = {"value": round(btf, 2), "unit": "TFLOP/s", "ms": round(bper[0], 4),
                            "workload": name, "flop_per_call": bflops,
                            "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel",
+                           "cpu_baseline": None if args.skip_cpu_baseline else cpu_sample(
+                               lambda: __import__("oracle").attention_backward(
+                                   q, k, v, do.cpu(), cfg.scale, cfg.causal, cfg.window,
+                                   heads=[(0, 0)]),
+                               bflops / (cfg.B * cfg.Hq),
+                               f"1 of {cfg.B * cfg.Hq} (batch, head) pairs of {name}, fp64 "
+                               "gradients of the materialised definition"),
                            "roofline": {"bound": "mfma", "achieved": round(btf, 2),
                                         "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                         "frac": round(btf / metrics.PEAK_BF16_TFLOPS, 4)}}
@@ -383,12 +410,21 @@ def main():
         padded = metrics.fwd_flops(len(lens), vc.Hq, vc.max_len, vc.max_len, vc.d, vc.causal,
                                    vc.window)
         vtf = vflops / (vper[0] * 1e-3) / 1e12
+        hq_, hk_, hv_ = pq.cpu(), pk.cpu(), pv.cpu()
+        hcu = cu_q.cpu().numpy()
         res["varlen"] = {"value": round(vtf, 2), "unit": "TFLOP/s", "ms": round(vper[0], 4),
                          "workload": vc.name, "num_seqs": int(len(lens)),
                          "mean_len": round(float(lens.mean()), 1), "max_len": int(lens.max()),
                          "flop_per_call": vflops,
                          "useful_fraction_if_padded": round(vflops / padded, 4),
                          "kernel": "fwd_bf16_kernel<128, varlen>",
+                         "cpu_baseline": None if args.skip_cpu_baseline else cpu_sample(
+                             lambda: __import__("oracle").attention_varlen(
+                                 hq_, hk_, hv_, hcu, hcu, vc.scale, vc.causal, vc.window,
+                                 seqs=list(range(16))),
+                             metrics.varlen_fwd_flops(lens[:16], lens[:16], vc.Hq, vc.d, vc.causal,
+                                                      vc.window),
+                             f"the first 16 of {len(lens)} sequences, all {vc.Hq} heads, fp64"),
                          "backward": {"value": round(2.5 * vflops / (vbper[0] * 1e-3) / 1e12, 2),
                                       "unit": "TFLOP/s", "ms": round(vbper[0], 4),
                                       "flop_per_call": 2.5 * vflops},
@@ -399,7 +435,8 @@ def main():
         print(f"bench: prefill over the paged cache {PREFILL_PAGED}", file=sys.stderr, flush=True)
         from exact_softmax_attention_amd import attn_prefill_paged
         ppc = workloads.PREFILL_PAGED_CONFIGS[PREFILL_PAGED]
-        pin = {kk: t.to(dev) for kk, t in workloads.make_prefill_paged_config(ppc).items()}
+        hpin = workloads.make_prefill_paged_config(ppc)
+        pin = {kk: t.to(dev) for kk, t in hpin.items()}
         ppout = torch.empty_like(pin["q"])
         pplse = torch.empty((ppc.Hq, pin["q"].shape[0]), dtype=torch.float32, device=dev)
         from exact_softmax_attention_amd import attn_prefill_paged_workspace_size
@@ -417,10 +454,23 @@ def main():
         pch = (pin["cu_seqlens_q"][1:] - pin["cu_seqlens_q"][:-1]).cpu().numpy()
         pflops = metrics.prefill_paged_flops(plens, pch, ppc.Hq, ppc.d, ppc.window)
         ptf = pflops / (pper[0] * 1e-3) / 1e12
+        smin = int(plens.argmin())
         res["prefill_paged"] = {"value": round(ptf, 2), "unit": "TFLOP/s", "ms": round(pper[0], 4),
                                 "workload": ppc.name, "new_tokens": int(pch.sum()),
                                 "cached_tokens": int(plens.sum()), "flop_per_call": pflops,
                                 "kernels": "fwd_bf16_kernel<128, paged> + prefill_merge_kernel<128>",
+                                "cpu_baseline": None if args.skip_cpu_baseline else cpu_sample(
+                                    lambda: __import__("oracle").prefill_paged(
+                                        hpin["q"], hpin["kcache"], hpin["vcache"],
+                                        hpin["block_table"], hpin["seq_lens"],
+                                        hpin["cu_seqlens_q"], ppc.scale, ppc.window,
+                                        seqs=[smin]),
+                                    metrics.prefill_paged_flops(plens[smin:smin + 1],
+                                                                pch[smin:smin + 1], ppc.Hq,
+                                                                ppc.d, ppc.window),
+                                    f"the shortest of {len(plens)} sequences ({int(plens[smin])} "
+                                    f"cached tokens, {int(pch[smin])} new), all {ppc.Hq} heads, "
+                                    "fp64"),
                                 "workspace_bytes": int(ppws.numel()),
                                 "roofline": {"bound": "mfma", "achieved": round(ptf, 2),
                                              "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
