@@ -14,6 +14,7 @@ computation runs in the library's HIP kernels; there is no fallback.
     attn_bwd(q, k, v, out, dout, lse, causal=False, window=0, scale=None)
     attn_bwd_workspace_size(B, Hq, Nq)
     attn_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, ...)
+    attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse=None)     merge of two partials
     attn_status_str(code)
 
 Layouts: q [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d]; out like q; lse [B, Hq, Nq]
@@ -41,6 +42,7 @@ __all__ = [
     "attn_bwd",
     "attn_bwd_workspace_size",
     "attn_bwd_varlen",
+    "attn_merge",
     "attn_status_str",
     "AttnError",
 ]
@@ -377,3 +379,37 @@ def attn_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, causal:
         workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "attn_bwd_varlen")
     return dq, dk, dv
+
+
+def attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, return_lse: bool = True):
+    """Exact merge of two partial results (O [B, N, H, d] bf16, LSE [B, H, N]
+    float32) of the same query rows over disjoint key sets.  out / lse may be
+    o_a / lse_a for an in-place merge.  Returns (out, lse)."""
+    for t, name in ((o_a, "o_a"), (o_b, "o_b")):
+        _dev(t, name, torch.bfloat16)
+    for t, name in ((lse_a, "lse_a"), (lse_b, "lse_b")):
+        _dev(t, name, torch.float32)
+    if o_a.dim() != 4 or o_b.shape != o_a.shape:
+        raise ValueError("o_a and o_b must be [B, N, H, d] of one shape")
+    B, N, H, d = o_a.shape
+    if lse_a.shape != (B, H, N) or lse_b.shape != (B, H, N):
+        raise ValueError("lse_a and lse_b must be [B, H, N]")
+    if out is None:
+        out = torch.empty_like(o_a)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if out.shape != o_a.shape:
+            raise ValueError("out must have o_a's shape")
+    if lse is None and return_lse:
+        lse = torch.empty_like(lse_a)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if lse.shape != lse_a.shape:
+            raise ValueError("lse must be [B, H, N]")
+    code = _lib.lib().attn_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(),
+                                 lse_b.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None, B, N, H, d,
+                                 _stream(o_a.device))
+    _check(code, "attn_merge")
+    return out, lse
+

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode_paged.hip", "bwd_bf16.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode_paged.hip", "bwd_bf16.hip", "merge.hip"]
 # The decode kernel multiplies its matrix-core accumulators by the softmax
 # rescale factor on the vector ALUs every block; keeping them in ordinary
 # VGPRs (rather than AGPRs) avoids copying them back and forth.

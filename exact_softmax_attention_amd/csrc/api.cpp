@@ -6,6 +6,7 @@
 #include <climits>
 
 #include "launch.h"
+#include "merge.h"
 
 namespace {
 
@@ -172,6 +173,18 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* out
                         Hkv,      d,        causal,     window > 0 ? window : 0,
                         scale,    workspace};
   const hipError_t e = attn::launch_bwd_bf16_varlen(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+int attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+               void* out, float* lse_out, int B, int N, int H, int d, void* stream) {
+  if (B < 0 || N < 0 || H < 1) return ATTN_E_SHAPE;
+  if (d != 64 && d != 128) return ATTN_E_HEADDIM;
+  if ((long long)B * N * H * d > (1LL << 40)) return ATTN_E_SHAPE;
+  if ((long long)B * N == 0) return ATTN_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !out) return ATTN_E_NULL;
+  attn::MergeArgs a{o_a, lse_a, o_b, lse_b, out, lse_out, B, N, H, d};
+  const hipError_t e = attn::launch_merge(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 

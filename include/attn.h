@@ -18,7 +18,10 @@
  *                            chunk) over the same paged cache;
  *   attn_bwd                 the gradients of attn_fwd (bf16), recomputing
  *                            the probabilities from the saved log-sum-exp;
- *   attn_bwd_varlen          the gradients of attn_fwd_varlen.
+ *   attn_bwd_varlen          the gradients of attn_fwd_varlen;
+ *   attn_merge               the exact merge of two partial results over
+ *                            disjoint key sets (the combine step of attention
+ *                            split along the keys, e.g. across devices).
  *
  * Sources (pages; section names as printed):
  *   - "Attention Is O(n^2): FlashAttention vs Linear Attention", "Why
@@ -42,7 +45,8 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; nothing is
  *     retained after the call returns.  Tensors are dense, row-major, with no
- *     padding.  Outputs must not alias inputs.
+ *     padding.  Outputs must not alias inputs (attn_merge alone allows an
+ *     in-place merge).
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL means the default stream).  The library never synchronises and
  *     never allocates device memory.
@@ -304,6 +308,28 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* out
                     const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
                     int total_q, int total_k, int Hq, int Hkv, int d, int causal, int window,
                     float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Exact merge of two partial results of the same query rows, each the
+ * attention of those rows over one of two disjoint key sets (as attn_fwd
+ * writes them): with w = exp(LSE - max(LSE_a, LSE_b)),
+ * O = (w_a O_a + w_b O_b) / (w_a + w_b) and LSE = max + ln(w_a + w_b)
+ * ("Ch. 3: MHA Limitations, MQA, GQA, and FlashAttention", 3.5: partial
+ * softmax states merge exactly after rescaling to a common maximum).  This
+ * is the combine step of attention split along the keys, e.g. a device of a
+ * ring that attends its queries to one K/V shard at a time ("How to Reduce
+ * Attention Computation Cost in LLM Training", ring attention section).
+ *
+ *   o_a, o_b, out        [B, N, H, d] bf16 (rounded to nearest even)
+ *   lse_a, lse_b         [B, H, N] float32; lse_out the same, or NULL
+ *
+ * out may be o_a and lse_out may be lse_a (an in-place running merge); no
+ * other overlap is allowed.  A row with LSE = -inf on both sides gets O = 0,
+ * LSE = -inf; a NaN LSE on either side gives NaN.  B, N >= 0, H >= 1, d in
+ * {64, 128}, B * N * H * d <= 2^40.
+ */
+int attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+               void* out, float* lse_out, int B, int N, int H, int d, void* stream);
 
 #ifdef __cplusplus
 }

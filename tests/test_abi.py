@@ -201,3 +201,13 @@ def test_bwd_varlen_validation():
     assert _bwdv(ws=None) == _lib.ATTN_E_WORKSPACE
     assert _bwdv(ws_bytes=16) == _lib.ATTN_E_WORKSPACE
     assert _bwdv(ptr=None, n=0) == _lib.ATTN_OK
+
+
+def test_merge_validation():
+    f = _lib.lib().attn_merge
+    p = 1 << 20
+    assert f(None, p, p, p, p, None, 1, 8, 2, 128, None) == _lib.ATTN_E_NULL
+    assert f(p, p, p, p, p, None, 1, 8, 0, 128, None) == _lib.ATTN_E_SHAPE
+    assert f(p, p, p, p, p, None, -1, 8, 2, 128, None) == _lib.ATTN_E_SHAPE
+    assert f(p, p, p, p, p, None, 1, 8, 2, 96, None) == _lib.ATTN_E_HEADDIM
+    assert f(None, None, None, None, None, None, 0, 8, 2, 128, None) == _lib.ATTN_OK
