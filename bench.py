@@ -36,6 +36,9 @@ fraction of a padded batch's work that would be useful (each sequence padded
 to 2048), and its backward (attn_bwd_varlen, 2.5x the forward's flops).
 --skip-varlen leaves both out.
 
+The merge of two partial results (attn_merge) at the prefill shape is reported
+under `merge` in GB/s of algorithmic bytes (two O and LSE read, one written).
+
 The fp32 single-head case (attn_fwd_f32, 1 x 256 x 1 x 64, non-causal) is
 timed in microseconds under `f32_single_head` (launch-latency bound).
 
@@ -476,6 +479,24 @@ def main():
                                              "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                              "frac": round(ptf / metrics.PEAK_BF16_TFLOPS, 4)}}
     if args.workload is None:
+        # the merge of two partial results at the prefill shape (one device's
+        # combine step when the keys are split into shards)
+        from exact_softmax_attention_amd import attn_merge
+        ob_, lb_ = out.clone(), lse.clone()
+        mo, ml = torch.empty_like(out), torch.empty_like(lse)
+
+        def merge():
+            attn_merge(out, lse, ob_, lb_, out=mo, lse=ml)
+
+        mper, _ = time_loop([merge], max(5, args.steps), max(2, args.warmup), torch)
+        mbytes = 3 * out.numel() * 2 + 3 * lse.numel() * 4
+        mgbs = mbytes / (mper[0] * 1e-3) / 1e9
+        res["merge"] = {"value": round(mgbs, 1), "unit": "GB/s", "ms": round(mper[0], 4),
+                        "workload": f"two partial results of {name}",
+                        "algorithmic_bytes": mbytes, "kernel": "merge_kernel<128>",
+                        "roofline": {"bound": "hbm", "achieved": round(mgbs, 1),
+                                     "peak": metrics.PEAK_HBM_GBS, "unit": "GB/s",
+                                     "frac": round(mgbs / metrics.PEAK_HBM_GBS, 4)}}
         # the fp32 single-head case (1 x 256 x 1 x 64): launch-latency bound,
         # reported in microseconds only
         from exact_softmax_attention_amd import attn_fwd_f32
