@@ -76,17 +76,22 @@ def test_merge_with_an_empty_side_is_exact():
 
 def test_merge_is_symmetric_and_propagates_nan():
     B, N, H, d = 1, 64, 2, 64
-    a = torch.randn(B, N, H, d).to(torch.bfloat16).cuda()
-    b = torch.randn(B, N, H, d).to(torch.bfloat16).cuda()
-    la = torch.randn(B, H, N).cuda()
-    lb = torch.randn(B, H, N).cuda()
+    g = torch.Generator().manual_seed(5200)
+    a = torch.randn(B, N, H, d, generator=g).to(torch.bfloat16).cuda()
+    b = torch.randn(B, N, H, d, generator=g).to(torch.bfloat16).cuda()
+    la = torch.randn(B, H, N, generator=g).cuda()
+    lb = torch.randn(B, H, N, generator=g).cuda()
     x, lx = attn_merge(a, la, b, lb)
     y, ly = attn_merge(b, lb, a, la)
     lb2 = lb.clone()
     lb2[0, 1, 5] = float("nan")
     z, lz = attn_merge(a, la, b, lb2)
     torch.cuda.synchronize()
-    assert torch.equal(x, y) and torch.equal(lx, ly)
+    # the LSE arithmetic is symmetric; O's weighted sum is contracted into an
+    # FMA whose rounding depends on the operand order, so it matches to one
+    # bf16 rounding
+    assert torch.equal(lx, ly)
+    assert (x.float() - y.float()).abs().max() <= 2 ** -7 * x.float().abs().max()
     assert torch.isnan(z[0, 5, 1].float()).all() and torch.isnan(lz[0, 1, 5])
     assert torch.isfinite(z[0, 5, 0].float()).all() and torch.isfinite(z[0, 4, 1].float()).all()
     # the merge formula itself, against the oracle's merge of (m, l, acc) states
