@@ -1,27 +1,37 @@
-"""The online softmax and the tiled recurrence, as the pages describe them.
+"""Partial softmax states and their exact merge; a key-blocked CPU model.
 
 Test infrastructure only (see the package docstring).
 
-* ``online_softmax`` follows "Modern Attention: MQA, GQA, FlashAttention,
-  Sliding Window and RoPE", section 3: one pass keeps a running maximum m and
-  a running denominator; when a new value raises the maximum the old
-  denominator is multiplied by exp(old m - new m).
-* ``tiled_attention_head`` follows "Attention Is O(n^2): FlashAttention vs
-  Linear Attention", section "FlashAttention - Same FLOPs, Linear Memory": an
-  outer loop over query blocks, an inner loop over K/V blocks, a running row
-  maximum and row sum, the accumulator rescaled by exp(old max - new max),
-  and one division by the running sum at the end.  Masked logits are -inf;
-  key blocks holding no visible key are skipped (they add nothing).
-* ``merge_states`` combines two partial softmax states (m, l, acc).  The
-  formula is missing from the extracted text of "Ch. 3", section 3.5 (only its
-  lead-in survives); it is reconstructed from the rescale step above:
-  M = max(m_a, m_b), l = l_a e^(m_a-M) + l_b e^(m_b-M), and the accumulator
-  scaled the same way.  It is exact algebra, since l e^m is invariant.
+The online softmax of "Modern Attention: MQA, GQA, FlashAttention, Sliding
+Window and RoPE", section 3, and the key-block loop of "Attention Is O(n^2):
+FlashAttention vs Linear Attention", section "FlashAttention - Same FLOPs,
+Linear Memory", rest on one fact: the softmax state of a set of logits,
+
+    m = max of the logits,   l = sum of exp(logit - m),
+    acc = sum of exp(logit - m) * value,
+
+can be formed for disjoint pieces separately and combined exactly, because
+l * e^m (and acc * e^m) is the same whatever reference maximum is used.  This
+module is written in those terms: a state per piece, an associative combine,
+and a fold.
+
+* ``merge_states`` is the combine: M = max(m_a, m_b), and l and acc are each
+  side rescaled by exp(m - M) and added.  The formula itself is missing from
+  the extracted text of "Ch. 3", section 3.5 (only its lead-in survives); this
+  is the rescale those pages describe, applied to two states.
+* ``online_softmax`` folds single-logit states (m = x, l = 1) with the
+  combine, which gives the page's running maximum and denominator after each
+  prefix; the probabilities are exp(x - m) / l.
+* ``tiled_attention_head`` forms one state per (query block, key block) from
+  that block's masked logits, skips key blocks with no visible key, and folds
+  each query block's states in key order.  It is a model of the GPU kernel's
+  tiling (which blocks are visited), checked against the plain definition.
 
 All arithmetic is float64.
 """
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -29,21 +39,8 @@ import numpy as np
 from .attention import _f64
 
 
-def online_softmax(xs):
-    """Softmax of a list by the one-pass recurrence.
-
-    Returns (probabilities, final running max, final running denominator).
-    """
-    m, den = -math.inf, 0.0
-    for x in xs:
-        new_m = max(m, x)
-        den = den * math.exp(m - new_m) + math.exp(x - new_m)
-        m = new_m
-    return [math.exp(x - m) / den for x in xs], m, den
-
-
 def _rescale(old_m, new_m):
-    """exp(old - new), taken as 0 where both are -inf (nothing seen yet)."""
+    """exp(old - new), taken as 0 where the new maximum is -inf (nothing seen)."""
     out = np.zeros_like(old_m)
     ok = np.isfinite(new_m)
     out[ok] = np.exp(old_m[ok] - new_m[ok])
@@ -60,9 +57,36 @@ def merge_states(a, b):
     return M, l_a * fa + l_b * fb, acc_a * fa[:, None] + acc_b * fb[:, None]
 
 
+def _logit_state(x: float):
+    """The state of a single logit: its own maximum, weight exp(0) = 1."""
+    return np.array([float(x)]), np.array([1.0]), np.zeros((1, 0))
+
+
+def online_softmax(xs):
+    """Softmax of a list as a fold of single-logit states.
+
+    Returns (probabilities, final maximum, final denominator).
+    """
+    empty = (np.array([-math.inf]), np.array([0.0]), np.zeros((1, 0)))
+    m, l, _ = functools.reduce(merge_states, map(_logit_state, xs), empty)
+    m, l = float(m[0]), float(l[0])
+    return [math.exp(x - m) / l for x in xs], m, l
+
+
+def _block_state(s, v):
+    """State of one block of masked logits s [R, C] (-inf = hidden) with its
+    values v [C, dv]: per row the block maximum, the sum of exp(s - max) and
+    the exp-weighted sum of the values."""
+    m = s.max(axis=1)
+    w = np.zeros_like(s)
+    live = np.isfinite(m)
+    w[live] = np.exp(s[live] - m[live, None])
+    return m, w.sum(axis=1), w @ v
+
+
 def tiled_attention_head(q, k, v, scale: float, causal: bool = False, window: int = 0,
                          block_q: int = 32, block_k: int = 32, return_stats: bool = False):
-    """Online-softmax attention for one head; q [Nq, d], k [Nk, d], v [Nk, dv].
+    """Key-blocked attention for one head; q [Nq, d], k [Nk, d], v [Nk, dv].
 
     Returns (O [Nq, dv], LSE [Nq]), plus the number of (query block, key
     block) pairs visited when ``return_stats``.
@@ -74,36 +98,27 @@ def tiled_attention_head(q, k, v, scale: float, causal: bool = False, window: in
     lse = np.full(Nq, -np.inf)
     visited = 0
     for i0 in range(0, Nq, block_q):
-        i1 = min(i0 + block_q, Nq)
-        pos = np.arange(i0, i1)[:, None] + delta
-        acc = np.zeros((i1 - i0, dv))
-        run_max = np.full(i1 - i0, -np.inf)
-        run_sum = np.zeros(i1 - i0)
+        rows = np.arange(i0, min(i0 + block_q, Nq))
+        pos = rows[:, None] + delta  # absolute positions (bottom-right causal)
+        states = []
         for j0 in range(0, Nk, block_k):
-            j1 = min(j0 + block_k, Nk)
-            j = np.arange(j0, j1)[None, :]
-            vis = np.ones((i1 - i0, j1 - j0), dtype=bool)
+            keys = np.arange(j0, min(j0 + block_k, Nk))[None, :]
+            vis = np.ones((rows.size, keys.size), dtype=bool)
             if causal:
-                vis &= j <= pos
+                vis &= keys <= pos
             if window > 0:
-                vis &= (pos - j) < window
+                vis &= (pos - keys) < window
             if not vis.any():
-                continue  # a block with no visible key changes nothing
+                continue  # a block with no visible key contributes nothing
             visited += 1
-            s = np.where(vis, (q[i0:i1] @ k[j0:j1].T) * scale, -np.inf)
-            new_max = np.maximum(run_max, s.max(axis=1))
-            p = np.zeros_like(s)
-            live = np.isfinite(new_max)
-            p[live] = np.exp(s[live] - new_max[live, None])
-            corr = _rescale(run_max, new_max)
-            run_sum = run_sum * corr + p.sum(axis=1)
-            acc = acc * corr[:, None] + p @ v[j0:j1]
-            run_max = new_max
-        live = run_sum > 0
-        out[i0:i1][live] = acc[live] / run_sum[live, None]
-        l_blk = np.full(i1 - i0, -np.inf)
-        l_blk[live] = run_max[live] + np.log(run_sum[live])
-        lse[i0:i1] = l_blk
+            s = np.where(vis, (q[rows] @ k[keys[0]].T) * scale, -np.inf)
+            states.append(_block_state(s, v[keys[0]]))
+        if not states:
+            continue  # rows that see no key: O = 0, LSE = -inf
+        m, l, acc = functools.reduce(merge_states, states)
+        live = l > 0
+        out[rows[live]] = acc[live] / l[live, None]
+        lse[rows[live]] = m[live] + np.log(l[live])
     if return_stats:
         return out, lse, visited
     return out, lse
