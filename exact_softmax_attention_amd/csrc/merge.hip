@@ -31,6 +31,12 @@ struct MergeParams {
   long long rows;  // B * N * H (row, head) pairs
 };
 
+// ca * xa + cb * xb with both products rounded to float before the add.
+__device__ __forceinline__ float sym_sum(float ca, float xa, float cb, float xb) {
+#pragma clang fp contract(off)
+  return ca * xa + cb * xb;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   constexpr int LPR = D / 8;  // lanes per (row, head): 16 bytes each
@@ -57,11 +63,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     const float sum = wa + wb;
     const float inv = nan ? __builtin_nanf("") : sum > 0.f ? 1.f / sum : 0.f;
     const float ca = wa * inv, cb = wb * inv;
+    // Each product is rounded on its own and then added (no contraction into
+    // an FMA, whose single rounding would depend on which side is the addend),
+    // so merge(a, b) and merge(b, a) agree bit for bit.
     u32x4 y;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      y[j] = pack_bf16x2(ca * bf16lo_to_f32(xa[j]) + cb * bf16lo_to_f32(xb[j]),
-                         ca * bf16hi_to_f32(xa[j]) + cb * bf16hi_to_f32(xb[j]));
+      y[j] = pack_bf16x2(sym_sum(ca, bf16lo_to_f32(xa[j]), cb, bf16lo_to_f32(xb[j])),
+                         sym_sum(ca, bf16hi_to_f32(xa[j]), cb, bf16hi_to_f32(xb[j])));
     *reinterpret_cast<u32x4*>(p.o + r * D + sub * 8) = y;
     if (sub == 0 && p.lse != nullptr)
       p.lse[li] = nan ? __builtin_nanf("") : sum > 0.f ? m + fast_log2(sum) * kLn2 : kNegInf;
