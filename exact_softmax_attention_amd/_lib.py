@@ -41,6 +41,7 @@ SIGNATURES = {
                              _I, _I, _F, _P, _SZ, _P]),
     "attn_merge": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
+    "attn_set_fwd_sched_slots": (_I, [_I]),
 }
 
 

@@ -244,6 +244,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+int attn_set_fwd_sched_slots(int n) { return attn::set_fwd_sched_slots(n); }
+
 const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

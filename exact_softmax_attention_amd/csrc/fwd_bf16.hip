@@ -101,7 +101,8 @@ struct Params {
   uint16_t* o;
   float* lse;
   int Hq, Hkv, group, Nq, Nk, causal, window, n_qtiles, total;
-  int slot;     // this launch's slot of scheduling counters
+  int slot;      // this launch's slot of scheduling counters
+  unsigned tag;  // and its tag (see claim_unit)
   int pairing;  // work units are pairs of query tiles (see the schedule)
   float sl2;  // scale * log2(e): scores are kept in the base-2 domain
   // packed sequences: boundaries of the query and key rows of each sequence,
@@ -146,13 +147,45 @@ __device__ __forceinline__ TileRange tile_range(int i0, int Nq, int Nk, int caus
   return r;
 }
 
-// Scheduling counters of the persistent kernel: slot s holds one item counter
-// per XCD and a count of finished work groups.  Launches take slots in turn,
-// so that launches in flight on different streams do not share counters; the
-// last work group of a launch returns its slot to zero.
+// Scheduling counters of the persistent kernel: slot s holds one unit counter
+// per XCD.  A counter is a 64-bit word, a launch's tag (high half) and the
+// next unit index (low half).  Every launch has its own tag (a host counter),
+// takes slot tag % kSchedSlots, and is preceded on its stream by a one-wave
+// kernel that sets the slot's counters to (tag, 0), so a launch replayed from
+// a captured graph starts afresh.  A work group claims a unit by
+// compare-and-swap and its claims only increase: it takes the counter's index
+// (or one past its own previous claim, if that is larger), and a counter that
+// carries another launch's tag (another launch in flight on the same slot) is
+// taken over at one past the group's previous claim.  Under this launch's
+// tag the indices handed out always form a prefix [0, max], so no unit is
+// skipped: a group leaves only after claiming an index past its range.
+// Sharing a slot makes launches repeat some units (each unit writes the same
+// values again), nothing more.
 constexpr int kXcds = 8;  // XCDs of the device; work group w runs on XCD w % 8
-constexpr int kSchedSlots = 64;
-__device__ int g_sched[kSchedSlots * (kXcds + 1)];
+constexpr int kSchedSlotsMax = 1024;
+__device__ unsigned long long g_sched[kSchedSlotsMax * kXcds];
+
+// Next unit index of this launch from counter `w`; `last` is this group's
+// previous claim (-1 before the first).
+__device__ __forceinline__ int claim_unit(unsigned long long* w, unsigned tag, int last) {
+  unsigned long long v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned next = (unsigned)(last + 1);
+  for (;;) {
+    const unsigned have = (unsigned)v;
+    const unsigned c = (unsigned)(v >> 32) == tag && have > next ? have : next;
+    const unsigned long long nv = ((unsigned long long)tag << 32) | (c + 1u);
+    const unsigned long long prev = atomicCAS(w, v, nv);
+    if (prev == v) return (int)c;
+    v = prev;
+  }
+}
+
+// Sets the counters of `slot` to (tag, 0) before the launch that uses them.
+__global__ __launch_bounds__(64) void sched_reset_kernel(int slot, unsigned tag) {
+  if (threadIdx.x < kXcds)
+    __hip_atomic_store(&g_sched[slot * kXcds + threadIdx.x], (unsigned long long)tag << 32,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Buffer resource for raw (unswizzled) 32-bit addressing: loads at byte
 // offsets >= bytes return zero and touch no memory.
@@ -292,12 +325,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   const int units = VARLEN ? p.total : p.total / nq * per_head;
   const int first = (int)((int64_t)units * groups_before / G);
   const int last = (int)((int64_t)units * (groups_before + Gx) / G);
-  int* const ctr = g_sched + p.slot * (kXcd + 1);  // [xcd counters..., finished groups]
-  if (tid == 0) s_unit = first + atomicAdd(ctr + xcd, 1);
+  unsigned long long* const ctr = g_sched + p.slot * kXcd + xcd;
+  int claimed = -1;  // thread 0: this group's latest claim
+  if (tid == 0) {
+    claimed = claim_unit(ctr, p.tag, claimed);
+    s_unit = first + claimed;
+  }
   __syncthreads();
   for (int unit = s_unit; unit < last;) {
   int grabbed = 0;  // the unit after this one, in flight meanwhile
-  if (tid == 0) grabbed = atomicAdd(ctr + xcd, 1);
+  if (tid == 0) {
+    claimed = claim_unit(ctr, p.tag, claimed);
+    grabbed = claimed;
+  }
   const int bh = unit / per_head;
   // pairs: the middle (costliest under a window) first; tiles: heavy first
   const int j = per_head - 1 - (unit - bh * per_head);
@@ -865,15 +905,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   __syncthreads();
   unit = s_unit;
   }
-  // The last group to finish returns this launch's counters to zero for the
-  // next launch that uses the same slot (every group's final take precedes
-  // its count of finished groups).
-  if (tid == 0) {
-    __threadfence();
-    if (atomicAdd(ctr + kXcd, 1) == G - 1) {
-      for (int x = 0; x <= kXcd; ++x) atomicExch(ctr + x, 0);
-    }
-  }
 }
 
 // Paged chunked prefill, second pass: rows of items done in several key
@@ -984,12 +1015,19 @@ long long fwd_bf16_grid(int B, int Hq, int Nq) {
 
 namespace {
 
-// one persistent work group per CU (the LDS ring admits one per CU); launches
-// take scheduling-counter slots in turn
+std::atomic<unsigned> g_launches{0};          // tags handed out so far
+std::atomic<int> g_sched_slots{kSchedSlotsMax};  // slots in use (tests may lower it)
+
+// one persistent work group per CU (the LDS ring admits one per CU); each
+// launch takes a fresh tag and the slot it names, whose counters a one-wave
+// kernel sets first
 template <int MODE>
 hipError_t launch(Params& p, int d, float scale, long long units, hipStream_t stream) {
-  static std::atomic<unsigned> launches{0};
-  p.slot = (int)(launches.fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
+  unsigned tag = g_launches.fetch_add(1, std::memory_order_relaxed) + 1u;
+  if (tag == 0) tag = g_launches.fetch_add(1, std::memory_order_relaxed) + 1u;  // 0 is no one's
+  p.tag = tag;
+  p.slot = (int)(tag % (unsigned)g_sched_slots.load(std::memory_order_relaxed));
+  hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, stream, p.slot, p.tag);
   const int cus = device_cus();
   const dim3 grid(units < cus ? (int)units : cus), block(kThreads);
   const bool pos = scale > 0.f;
@@ -1008,6 +1046,12 @@ hipError_t launch(Params& p, int d, float scale, long long units, hipStream_t st
 }
 
 }  // namespace
+
+int set_fwd_sched_slots(int n) {
+  const int prev = g_sched_slots.load();
+  if (n >= 1 && n <= kSchedSlotsMax) g_sched_slots.store(n);
+  return prev;
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   Params p{};

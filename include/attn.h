@@ -64,11 +64,20 @@
  *   - LSE is the natural logarithm of sum_j exp(scale * q.k_j) over the
  *     visible keys, in float32.
  *   - `scale` is used as given (callers normally pass 1/sqrt(d)).
- *   - The library is thread-safe.  Its only state is a per-device cache of the
- *     compute-unit count, filled on first use, and the forward kernel's
- *     scheduling counters in device memory: 64 slots that launches take in
- *     turn, each returned to zero by the launch that used it, so up to 64
- *     forward launches may be in flight at once (on any streams).
+ *   - The library is thread-safe.  Its state is a per-device cache of the
+ *     compute-unit count, filled on first use, and the scheduling counters of
+ *     the bf16 forward kernels (attn_fwd, attn_fwd_varlen, attn_prefill_paged)
+ *     in device memory: each launch takes a fresh tag and one of 1024 counter
+ *     slots in turn, and is preceded on its stream by a one-wave kernel that
+ *     sets that slot to its tag.  Launches in flight on different slots are
+ *     independent.  Two launches running at once on the same slot (1024 or
+ *     more in flight) still compute their results exactly, but may repeat
+ *     work units.
+ *   - Graph capture: a forward call records two kernel launches (the counter
+ *     set-up and the kernel); the tag is fixed in the captured launch, and
+ *     every replay sets its slot afresh, so replays in turn are correct.
+ *     Replays of one captured call must not overlap each other (they also
+ *     write the same outputs).
  */
 #ifndef ATTN_MI355X_ATTN_H
 #define ATTN_MI355X_ATTN_H
@@ -94,6 +103,17 @@ enum {
 /*
  * Prefill / training forward, bf16 in and out, float32 accumulation.
  *
+ * Defines: O = softmax(scale * Q K^T + mask) V per (batch, query head)
+ * ("Attention Is O(n^2): FlashAttention vs Linear Attention", "Why Attention
+ * Is O(n^2)"), computed by the query-block / key-block loop of that page's
+ * "FlashAttention - Same FLOPs, Linear Memory" (running maximum and sum,
+ * rescale, final division; the float32 log-sum-exp is kept for the backward
+ * pass); grouped K/V heads as in "Ch. 3: MHA Limitations, MQA, GQA, and
+ * FlashAttention", 3.3; the sliding window of "Modern Attention: MQA, GQA,
+ * FlashAttention, Sliding Window and RoPE", 4; the (B, N, H, d) bf16 layout of
+ * the fused call in "How to Reduce Attention Computation Cost in LLM
+ * Training", "FlashAttention Is Table Stakes Now".
+ *
  *   q    [B, Nq, Hq, d]   bf16
  *   k, v [B, Nk, Hkv, d]  bf16
  *   out  [B, Nq, Hq, d]   bf16 (rounded to nearest even)
@@ -113,7 +133,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 /*
  * The same operation on float32 q, k, v and out, with float32 products and
  * accumulation throughout (no reduced-precision matrix formats).  Parameters
- * and rules are those of attn_fwd.
+ * and rules are those of attn_fwd.  Defines the same result: the definition
+ * in "Attention Is O(n^2): FlashAttention vs Linear Attention", "Why
+ * Attention Is O(n^2)", whose "Wall-Clock Impact of Tiling" runs it at d = 64
+ * with float inputs; the online softmax of "Modern Attention: MQA, GQA,
+ * FlashAttention, Sliding Window and RoPE", 3 (its worked example is one of
+ * this entry point's tests).
  */
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse,
                  int B, int Hq, int Hkv, int Nq, int Nk, int d,
@@ -161,6 +186,14 @@ size_t attn_decode_paged_workspace_size(int B, int Hq, int d, int block_size,
 
 /*
  * Single-query decode over a block-paged KV cache.
+ *
+ * Defines: for each sequence, the attention of its newest token's query over
+ * every cached key and value of that sequence, its own K/V included ("Ch. 3:
+ * MHA Limitations, MQA, GQA, and FlashAttention", 3.1: each new query reads
+ * the historical K/V, its own appended first); the cache is split into
+ * fixed-size blocks reached through a lookup table ("Inference Engineering",
+ * 2.5 "Optimizing Attention", PagedAttention); the keys are processed in
+ * pieces whose partial softmax states are merged exactly ("Ch. 3", 3.5).
  *
  *   q            [B, Hq, d] bf16: the query of the token at position
  *                seq_lens[b] - 1, whose own K/V are already in the cache
@@ -284,6 +317,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
 
 /* Static, human-readable text for a status code. */
 const char* attn_status_str(int status);
+
+/*
+ * Testing hook: the number of scheduling-counter slots the bf16 forward
+ * launches cycle through (1 .. 1024, default 1024; other values leave it
+ * unchanged).  Returns the previous number.  Fewer slots make concurrent
+ * launches share counters, which exercises the shared-slot path; results
+ * do not change.  Host state only; no HIP call.
+ */
+int attn_set_fwd_sched_slots(int n);
 
 /*
  * Gradients of attn_fwd_varlen (packed sequences; "How to Reduce Attention

@@ -210,16 +210,12 @@ def test_paired_schedule_odd_query_tiles():
         check(out[b, rows, h], O, lse[b, h, rows], L, "bf16", f"paired b{b} h{h}")
 
 
-def test_persistent_queue_reuse_and_streams():
-    """The persistent kernel takes its work from counters that live across
-    launches (a ring of 64 slots, each returned to zero by its launch).  Many
-    launches in a row, of shapes that alternate between the paired and the
-    single-tile schedules, and launches in flight on two streams at once must
-    all reproduce the result of a lone launch bit for bit."""
+def _sched_inputs():
     shapes = [
-        (4, 32, 8, 8192, 8192, 128, True, 0),   # paired query tiles
+        (4, 32, 8, 8192, 8192, 128, True, 0),   # paired query tiles, a long launch
         (1, 4, 2, 700, 700, 64, True, 0),       # single tiles
         (2, 8, 8, 1500, 1500, 128, False, 0),
+        (1, 8, 2, 3000, 3000, 128, True, 1000),
     ]
     inputs, refs = [], []
     for i, (B, Hq, Hkv, Nq, Nk, d, causal, w) in enumerate(shapes):
@@ -227,21 +223,63 @@ def test_persistent_queue_reuse_and_streams():
         qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
         inputs.append((qd, kd, vd, causal, w))
         refs.append(attn_fwd(qd, kd, vd, causal=causal, window=w))
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    return inputs, refs
+
+
+def test_persistent_queue_reuse_and_streams():
+    """The persistent kernel takes its work from counters in device memory that
+    launches reuse: each launch takes a fresh tag and a slot, set up by a
+    one-wave kernel before it.  Many launches in a row, of shapes that
+    alternate between the paired and the single-tile schedules, and 4 streams
+    with 20 launches each in flight at once must all reproduce the result of
+    a lone launch bit for bit."""
+    inputs, refs = _sched_inputs()
     for it in range(70):
-        s = it % len(shapes)
+        s = it % len(inputs)
         qd, kd, vd, causal, w = inputs[s]
         out, lse = attn_fwd(qd, kd, vd, causal=causal, window=w)
         torch.cuda.synchronize()
         assert torch.equal(out, refs[s][0]) and torch.equal(lse, refs[s][1]), f"launch {it}"
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    for rep in range(4):
-        results = []
-        for s, st in enumerate(streams):
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    results = []
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for it in range(20):
+        for j, st in enumerate(streams):
+            s = (it + j) % len(inputs)
             qd, kd, vd, causal, w = inputs[s]
-            st.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(st):
-                results.append(attn_fwd(qd, kd, vd, causal=causal, window=w))
+                results.append((s, attn_fwd(qd, kd, vd, causal=causal, window=w)))
+    torch.cuda.synchronize()
+    for n, (s, (out, lse)) in enumerate(results):
+        assert torch.equal(out, refs[s][0]) and torch.equal(lse, refs[s][1]), f"launch {n} shape {s}"
+
+
+def test_shared_counter_slot_still_exact():
+    """With a single counter slot every launch shares it: one long launch on
+    one stream and 70 short launches of two shapes on another, in flight
+    together, take over each other's counters.  Work may be repeated, but every
+    launch must still reproduce a lone launch bit for bit."""
+    from exact_softmax_attention_amd import _lib
+    inputs, refs = _sched_inputs()
+    prev = _lib.lib().attn_set_fwd_sched_slots(1)
+    try:
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        a.wait_stream(torch.cuda.current_stream())
+        b.wait_stream(torch.cuda.current_stream())
+        qd, kd, vd, causal, w = inputs[0]
+        with torch.cuda.stream(a):
+            long_res = attn_fwd(qd, kd, vd, causal=causal, window=w)
+        short = []
+        for it in range(70):
+            s = 1 + it % 3
+            qd, kd, vd, causal, w = inputs[s]
+            with torch.cuda.stream(b):
+                short.append((s, attn_fwd(qd, kd, vd, causal=causal, window=w)))
         torch.cuda.synchronize()
-        for s, (out, lse) in enumerate(results):
-            assert torch.equal(out, refs[s][0]) and torch.equal(lse, refs[s][1]), f"stream {s} rep {rep}"
+    finally:
+        _lib.lib().attn_set_fwd_sched_slots(prev)
+    assert torch.equal(long_res[0], refs[0][0]) and torch.equal(long_res[1], refs[0][1])
+    for n, (s, (out, lse)) in enumerate(short):
+        assert torch.equal(out, refs[s][0]) and torch.equal(lse, refs[s][1]), f"short {n} shape {s}"
