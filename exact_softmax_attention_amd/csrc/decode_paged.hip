@@ -8,12 +8,15 @@
 // "Ch. 3", 3.5: l e^m is invariant, so states rescaled to a common maximum
 // add).
 //
-// Work split.  All cache blocks the batch reads (for one KV head) are laid end
-// to end, sequence after sequence, and cut into W equal ranges, one per wave,
-// so every wave streams the same number of blocks whatever the length mix; a
-// range that crosses a sequence boundary yields one partial state per
-// sequence it touches.  A wave serves one KV head and up to 16 of the query
-// heads that share it.
+// Work split.  All cache blocks the batch reads are laid end to end, sequence
+// after sequence, and cut into W equal ranges, so every wave streams the same
+// number of blocks whatever the length mix; a range that crosses a sequence
+// boundary yields one partial state per sequence it touches.  A wave serves
+// one KV head and up to 16 of the query heads that share it.  The waves of a
+// work group take the same range for up to 8 consecutive (KV head, head
+// group) pairs, so they read the same cache blocks side by side: a block's
+// token rows hold all KV heads next to each other, and the group's waves
+// together read them whole and at the same time.
 //
 // Kernel 1 (split), per 16-token block, all on the matrix cores:
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, A = 16 key rows straight from
@@ -42,8 +45,9 @@ namespace {
 constexpr int kBlock = 16;         // tokens per cache block
 constexpr float kLazy = 8.0f;      // rescale only when a score passes max + 8 (base 2)
 constexpr int kCombineWaves = 4;
-constexpr int kMaxWaves = 1024;    // waves per (KV head, head group): bounds the workspace
+constexpr int kMaxRanges = 512;    // block ranges (work groups along x): bounds the workspace
 constexpr int kWavesPerSimd = 2;   // resident split waves per SIMD (register bound)
+constexpr int kGroupWaves = 8;     // most (KV head, head group) pairs in one work group
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -56,10 +60,11 @@ struct Params {
   const int* lens;
   uint16_t* o;
   float* lse;
-  float2* ws_ml;   // [Hq, kMaxWaves + B] (m, l); slot of (wave w, sequence b) = w + b
-  float* ws_acc;   // [Hq, kMaxWaves + B, D]
-  int2* ws_seq;    // [B] (first wave, last wave) covering the sequence
+  float2* ws_ml;   // [Hq, kMaxRanges + B] (m, l); slot of (range w, sequence b) = w + b
+  float* ws_acc;   // [Hq, kMaxRanges + B, D]
+  int2* ws_seq;    // [B] (first range, last range) covering the sequence
   int B, Hq, Hkv, group, hgroups, max_blocks, num_blocks, window, W, slots;
+  int pairs, gwaves;  // (KV head, head group) pairs, and pairs per work group
   float sl2;
 };
 
@@ -85,23 +90,27 @@ struct DecTile {
 };
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
+__global__ __launch_bounds__(64 * kGroupWaves) void decode_split_kernel(const Params p) {
   using T = DecTile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t vs[kBlock * T::PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_all[kGroupWaves][kBlock * T::PITCH];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int pair = blockIdx.y * p.gwaves + wv;  // (KV head, head group) of this wave
+  if (pair >= p.pairs) return;  // no barriers below: the group's waves are independent
+  uint16_t* const vs = vs_all[wv];
   const int n = lane & 15;   // MFMA column: query head; also the K token row
   const int g = lane >> 4;   // MFMA k-group
   const int w = blockIdx.x;
-  const int hk = blockIdx.y / p.hgroups;
-  const int hsub = (blockIdx.y % p.hgroups) * 16;  // first head of this wave within the group
+  const int hk = pair / p.hgroups;
+  const int hsub = (pair % p.hgroups) * 16;  // first head of this wave within the group
   const int nh = min(16, p.group - hsub);          // heads this wave serves
   const int h0 = hk * p.group + hsub;
 
   // Blocks of all sequences laid end to end: C_b = blocks before sequence b,
   // T = all blocks.  A wave-wide prefix sum, 64 sequences at a time, finds the
   // total and the sequence holding this wave's first block.
-  int total = 0;
+  int total = 0;  // (the same in every wave of the grid)
   for (int c = 0; c < p.B; c += 64) {
     const int j = c + lane;
     int x = j < p.B ? seq_blocks(p.lens[j], p.max_blocks, p.window) : 0;
@@ -109,8 +118,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
     for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
     total += x;
   }
-  // never more waves than blocks, so that every working wave owns at least one
-  // block and the waves covering a sequence are consecutive and all write a partial
+  // never more ranges than blocks, so that every range owns at least one block
+  // and the ranges covering a sequence are consecutive and all write a partial
   const int nw = min(p.W, total);
   if (w >= nw) return;
   const int g0 = (int)((int64_t)w * total / nw);
@@ -142,7 +151,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
   const int vrow = lane / T::RL;
   const int vcol = 8 * (lane % T::RL);
   const int64_t voff = (int64_t)vrow * row_elems + hk * D + vcol;
-  const uint32_t vs_base = (uint32_t)(uintptr_t)vs;
+  const uint32_t vs_base = (uint32_t)(uintptr_t)vs;  // this wave's staging rows
   const int sl = lane & 15;
   // transposing-read address: lane (sl, g) supplies row 4g + sl/4, features 4(sl%4) ..+3
   const uint32_t rd = vs_base + 2u * (uint32_t)((4 * g + (sl >> 2)) * T::PITCH + 4 * (sl & 3));
@@ -287,8 +296,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const Params p) {
         p.ws_ml[slot] = any_bad ? make_float2(__builtin_nanf(""), __builtin_nanf(""))
                                 : make_float2(m, lsum);
     }
-    // the waves holding a sequence's first and last blocks record themselves
-    if (hk == 0 && hsub == 0 && lane == 0) {
+    // the ranges holding a sequence's first and last blocks record themselves
+    if (pair == 0 && lane == 0) {
       if (gpos == cb) p.ws_seq[b].x = w;
       if (end == cb + nb) p.ws_seq[b].y = w;
     }
@@ -318,7 +327,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(cons
     if (tid == 0 && p.lse != nullptr) p.lse[(int64_t)b * p.Hq + hq] = __builtin_nanf("");
     return;
   }
-  // partials of this sequence: slots w + b for the waves w that covered it
+  // partials of this sequence: slots w + b for the ranges w that covered it
   int s0 = 0, s1 = 0;
   if (seq_blocks(L, p.max_blocks, p.window) > 0) {
     const int2 fl = p.ws_seq[b];
@@ -399,7 +408,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(cons
 size_t decode_workspace_bytes(int B, int Hq, int d, int block_size, int max_blocks_per_seq) {
   (void)block_size;
   (void)max_blocks_per_seq;
-  const size_t slots = (size_t)Hq * (kMaxWaves + B);
+  const size_t slots = (size_t)Hq * (kMaxRanges + B);
   const size_t seq = ((size_t)B * sizeof(int2) + 255) / 256 * 256;
   const size_t ml = (slots * sizeof(float2) + 255) / 256 * 256;
   return seq + ml + slots * (size_t)d * sizeof(float);
@@ -425,11 +434,14 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
   p.num_blocks = a.num_blocks;
   p.window = a.window;
   p.sl2 = a.scale * kLog2e;
-  // one wave per resident slot of the whole GPU, shared by the (KV head, head group) pairs
-  const int pairs = a.Hkv * p.hgroups;
+  // one wave per resident slot of the whole GPU: W block ranges, each taken by
+  // ceil(pairs / gwaves) work groups of up to 8 waves
+  p.pairs = a.Hkv * p.hgroups;
+  p.gwaves = p.pairs < kGroupWaves ? p.pairs : kGroupWaves;
+  const int ygroups = (p.pairs + p.gwaves - 1) / p.gwaves;
   const int resident = device_cus() * 4 * kWavesPerSimd;
-  p.W = max(1, min(kMaxWaves, resident / pairs));
-  p.slots = kMaxWaves + a.B;
+  p.W = max(1, min(kMaxRanges, resident / (p.gwaves * ygroups)));
+  p.slots = kMaxRanges + a.B;
   char* ws = static_cast<char*>(a.workspace);
   const size_t seq_bytes = ((size_t)a.B * sizeof(int2) + 255) / 256 * 256;
   const size_t slots = (size_t)a.Hq * p.slots;
@@ -438,11 +450,11 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
   p.ws_ml = reinterpret_cast<float2*>(ws + seq_bytes);
   p.ws_acc = reinterpret_cast<float*>(ws + seq_bytes + ml_bytes);
 
-  const dim3 grid1(p.W, pairs);
+  const dim3 grid1(p.W, ygroups);
   if (a.d == 128)
-    hipLaunchKernelGGL(decode_split_kernel<128>, grid1, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_split_kernel<128>, grid1, dim3(64 * p.gwaves), 0, stream, p);
   else
-    hipLaunchKernelGGL(decode_split_kernel<64>, grid1, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_split_kernel<64>, grid1, dim3(64 * p.gwaves), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid2(a.Hq, a.B);

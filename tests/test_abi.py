@@ -64,10 +64,10 @@ def test_fwd_validation(fn):
 def test_decode_workspace_size():
     L = _lib.lib()
     n = L.attn_decode_paged_workspace_size(16, 32, 128, 16, 2000)
-    # per query head: one (m, l) pair and d floats for each of up to 1024 waves
-    # plus one per sequence (a wave's range may end inside a sequence), and a
-    # (first, last) wave pair per sequence
-    slots = 32 * (1024 + 16)
+    # per query head: one (m, l) pair and d floats for each of up to 512 block
+    # ranges plus one per sequence (a range may end inside a sequence), and a
+    # (first, last) range pair per sequence
+    slots = 32 * (512 + 16)
     assert n >= slots * (128 * 4 + 8) + 16 * 8
     assert n < slots * (128 * 4 + 8) + 16 * 8 + 1024
     assert L.attn_decode_paged_workspace_size(16, 32, 128, 32, 2000) == 0   # block size
