@@ -51,6 +51,13 @@ carry their own `cpu_baseline`: the fp64 oracle timed on a bounded sample of
 that workload (one head, sixteen sequences, one sequence), scaled by the
 sample's flops.
 
+The other dense configurations are timed alone after the step and reported
+as objects of their own, each with TFLOP/s (causal- or window-adjusted
+flops), its roofline fraction and a `cpu_baseline` (the oracle on 2 (batch,
+head) pairs, scaled): `gqa_causal_16k` (B=2, Hq=32, Hkv=8, N=16384),
+`mqa_causal_16k` (Hkv=1) and `swa_causal_32k_w4096` (B=1, Hq=32, Hkv=8,
+N=32768, W=4096).  --skip-dense-extra leaves them out.
+
 Other workloads can be timed with --workload NAME (one of the dense configs);
 the default line is the one described above.
 """
@@ -106,8 +113,12 @@ def parse():
     ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--skip-varlen", action="store_true")
     ap.add_argument("--skip-prefill-paged", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
-                    help="copy: a plain device copy of known size (counter calibration)")
+    ap.add_argument("--skip-dense-extra", action="store_true",
+                    help="leave out the GQA/MQA 16K and sliding-window 32K objects")
+    ap.add_argument("--mode", choices=["bench", "copy", "stream"], default="bench",
+                    help="copy: a plain device copy of known size (counter calibration); "
+                         "stream: a contiguous read of the decode workload's byte count "
+                         "(the memory system's rate for a plain streaming read)")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic.json from rocprofv3 --pmc runs under DIR "
                          "(no GPU needed)")
@@ -216,6 +227,45 @@ def cpu_sample(fn, flops, sample):
             "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
 
 
+EXTRA_DENSE = ("gqa_causal_16k", "mqa_causal_16k", "swa_causal_32k_w4096")
+
+
+def dense_object(name, args, torch, dev):
+    """One more dense forward workload, timed alone: TFLOP/s, roofline, CPU baseline."""
+    import workloads
+    from exact_softmax_attention_amd import attn_fwd, metrics
+    cfg = workloads.DENSE_CONFIGS[name]
+    print(f"bench: {name}", file=sys.stderr, flush=True)
+    q, k, v = workloads.make_dense_config(cfg)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.Nq), dtype=torch.float32, device=dev)
+
+    def fwd():
+        attn_fwd(qd, kd, vd, causal=cfg.causal, window=cfg.window, scale=cfg.scale, out=out,
+                 lse=lse)
+
+    per, _ = time_loop([fwd], args.steps, args.warmup, torch)
+    flops = metrics.fwd_flops(cfg.B, cfg.Hq, cfg.Nq, cfg.Nk, cfg.d, cfg.causal, cfg.window)
+    tf = flops / (per[0] * 1e-3) / 1e12
+    obj = {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(per[0], 4),
+           "config": {"B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.Nq, "d": cfg.d,
+                      "causal": cfg.causal, "window": cfg.window, "seed": cfg.seed},
+           "flop_per_launch": flops,
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2),
+                        "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / metrics.PEAK_BF16_TFLOPS, 4),
+                        "traffic": measured_traffic(f"fwd:{name}", FWD_FILES),
+                        "kernel": "fwd_bf16_kernel<128>",
+                        "algorithmic_bytes": metrics.fwd_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq,
+                                                               cfg.Nk, cfg.d)}}
+    del qd, kd, vd, out, lse
+    torch.cuda.empty_cache()
+    if not args.skip_cpu_baseline:
+        obj["cpu_baseline"] = cpu_baseline(q, k, v, cfg, n_heads=2)
+    return obj
+
+
 def time_loop(fns, steps, warmup, torch):
     """Run each fn once per step; per-fn average ms from HIP events, total wall ms."""
     for _ in range(warmup):
@@ -266,6 +316,26 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n,
                           "launches": max(1, args.steps)}))
+        return
+
+    if args.mode == "stream":
+        # the decode workload's algorithmic bytes, read once contiguously by a
+        # reduction (torch's own kernel): what a plain streaming read reaches
+        import workloads as _w
+        pc = _w.PAGED_CONFIGS[DECODE]
+        lens = _w.paged_seq_lens(pc)
+        nbytes = metrics.decode_bytes(lens, pc.Hq, pc.Hkv, pc.d, pc.block_size)
+        x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+        acc = torch.empty((), dtype=torch.float32, device=dev)
+
+        def rd():
+            torch.sum(x, dim=0, dtype=torch.float32, out=acc)
+
+        per, _ = time_loop([rd], max(5, args.steps), max(2, args.warmup), torch)
+        print(json.dumps({"mode": "stream", "bytes": int(x.numel() * 2), "ms": round(per[0], 4),
+                          "GB/s": round(x.numel() * 2 / (per[0] * 1e-3) / 1e9, 1),
+                          "of_peak": round(x.numel() * 2 / (per[0] * 1e-3) / 1e9
+                                           / metrics.PEAK_HBM_GBS, 4)}))
         return
 
     name = args.workload or PREFILL
@@ -512,6 +582,10 @@ def main():
         res["f32_single_head"] = {"us": round(fper[0] * 1e3, 2), "workload": fc.name,
                                   "kernel": "fwd_f32_kernel<64>",
                                   "note": "launch-latency bound; no roofline fraction"}
+    if args.workload is None and not args.skip_dense_extra:
+        # the other dense configurations: GQA and MQA causal 16K, sliding window 32K
+        for nm in EXTRA_DENSE:
+            res[nm] = dense_object(nm, args, torch, dev)
     if not args.skip_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(q, k, v, cfg)

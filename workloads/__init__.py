@@ -357,6 +357,12 @@ def make_paged(B: int, Hq: int, Hkv: int, d: int, block_size: int, num_blocks: i
     }
 
 
+def paged_seq_lens(cfg: PagedConfig):
+    """The sequence lengths make_paged_config draws (its generator's first draw)."""
+    rng = np.random.default_rng(cfg.seed)
+    return rng.integers(cfg.len_lo, cfg.len_hi, size=cfg.B, endpoint=True).astype(np.int64)
+
+
 def make_paged_config(cfg: PagedConfig, poison: bool = True):
     return make_paged(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.block_size, cfg.num_blocks,
                       cfg.max_blocks_per_seq, cfg.seed, cfg.len_lo, cfg.len_hi,
