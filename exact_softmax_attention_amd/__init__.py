@@ -36,6 +36,7 @@ __all__ = [
     "attn_fwd_f32",
     "attn_fwd_varlen",
     "attn_decode_paged",
+    "attn_decode_paged_noalloc",
     "attn_decode_paged_workspace_size",
     "attn_prefill_paged",
     "attn_prefill_paged_workspace_size",
@@ -222,6 +223,46 @@ def attn_decode_paged(q, kcache, vcache, block_table, seq_lens, scale=None, wind
         B, Hq, Hkv, d, block_size, max_blocks, num_blocks, int(window), float(scale),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "attn_decode_paged")
+    return out, lse
+
+
+def attn_decode_paged_noalloc(q, kcache, vcache, block_table, seq_lens, scale=None,
+                              window: int = 0, out=None, lse=None, return_lse: bool = True):
+    """attn_decode_paged with the library's own scratch array (no workspace).
+
+    Calls that overlap in time on one GPU must not be made (they share it).
+    """
+    _dev(q, "q", torch.bfloat16)
+    _dev(kcache, "kcache", torch.bfloat16)
+    _dev(vcache, "vcache", torch.bfloat16)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 3 or kcache.dim() != 4 or vcache.shape != kcache.shape:
+        raise ValueError("expected q [B,Hq,d] and caches [num_blocks,block_size,Hkv,d]")
+    B, Hq, d = q.shape
+    num_blocks, block_size, Hkv, dk = kcache.shape
+    if dk != d:
+        raise ValueError("q and the cache disagree on the head dimension")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    code = _lib.lib().attn_decode_paged_noalloc(
+        q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        B, Hq, Hkv, d, block_size, block_table.shape[1], num_blocks, int(window), float(scale),
+        _stream(q.device))
+    _check(code, "attn_decode_paged_noalloc")
     return out, lse
 
 

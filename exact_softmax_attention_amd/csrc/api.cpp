@@ -196,11 +196,13 @@ size_t attn_decode_paged_workspace_size(int B, int Hq, int d, int block_size,
   return attn::decode_workspace_bytes(B, Hq, d, block_size, max_blocks_per_seq);
 }
 
-int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
-                      const int* block_table, const int* seq_lens, void* out, float* lse, int B,
-                      int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
-                      int num_blocks, int window, float scale, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int check_decode(const void* q, const void* kcache, const void* vcache, const int* block_table,
+                 const int* seq_lens, const void* out, int B, int Hq, int Hkv, int d,
+                 int block_size, int max_blocks_per_seq, int num_blocks) {
   int st = check_common(B, Hq, Hkv, d);
   if (st != ATTN_OK) return st;
   if (B > 0 && (!q || !kcache || !vcache || !block_table || !seq_lens || !out))
@@ -210,6 +212,21 @@ int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
   if (B > 65535 || Hq > 65535) return ATTN_E_SHAPE;  // grid y limits
   // block counts of the whole batch are summed in 32-bit integers on the device
   if ((long long)B * max_blocks_per_seq > INT_MAX) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
+                      const int* block_table, const int* seq_lens, void* out, float* lse, int B,
+                      int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
+                      int num_blocks, int window, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const int st = check_decode(q, kcache, vcache, block_table, seq_lens, out, B, Hq, Hkv, d,
+                              block_size, max_blocks_per_seq, num_blocks);
+  if (st != ATTN_OK) return st;
   if (B == 0) return ATTN_OK;
   const size_t need = attn::decode_workspace_bytes(B, Hq, d, block_size, max_blocks_per_seq);
   if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
@@ -217,6 +234,25 @@ int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
                      B,  Hq,     Hkv,    d,           block_size, max_blocks_per_seq,
                      num_blocks, window > 0 ? window : 0, scale, workspace};
   const hipError_t e = attn::launch_decode_paged(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+int attn_decode_paged_noalloc(const void* q, const void* kcache, const void* vcache,
+                              const int* block_table, const int* seq_lens, void* out, float* lse,
+                              int B, int Hq, int Hkv, int d, int block_size,
+                              int max_blocks_per_seq, int num_blocks, int window, float scale,
+                              void* stream) {
+  const int st = check_decode(q, kcache, vcache, block_table, seq_lens, out, B, Hq, Hkv, d,
+                              block_size, max_blocks_per_seq, num_blocks);
+  if (st != ATTN_OK) return st;
+  if (B == 0) return ATTN_OK;
+  if (attn::decode_workspace_bytes(B, Hq, d, block_size, max_blocks_per_seq) >
+      attn::decode_scratch_bytes())
+    return ATTN_E_WORKSPACE;
+  attn::DecodeArgs a{q,  kcache, vcache, block_table, seq_lens, out, lse,
+                     B,  Hq,     Hkv,    d,           block_size, max_blocks_per_seq,
+                     num_blocks, window > 0 ? window : 0, scale, nullptr};
+  const hipError_t e = attn::launch_decode_paged_noalloc(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 

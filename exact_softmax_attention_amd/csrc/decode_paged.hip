@@ -465,4 +465,41 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---- Decode without a caller workspace.  The partials live in this file's
+// own device array (each GPU the library runs on holds one, from module load
+// until the process ends).  Host code never passes the array's name to a
+// kernel: that name is a host-side stand-in, not a device address.  The first
+// call on each device looks the address up with hipGetSymbolAddress (that
+// device current) and keeps it; every later call uses the kept pointer.
+// Nothing in the array needs to start at zero (the kernels write every value
+// they read), and all calls on one GPU share it, so calls that overlap on one
+// GPU race.
+
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;  // 16 MiB per device
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_decode_paged_noalloc(const DecodeArgs& args, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    // racing first calls on one device store the same address
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  DecodeArgs a = args;
+  a.workspace = ptr;
+  return launch_decode_paged(a, stream);
+}
+
 }  // namespace attn

@@ -132,5 +132,10 @@ hipError_t launch_bwd_bf16_varlen(const BwdVarlenArgs& a, hipStream_t stream);
 
 size_t decode_workspace_bytes(int B, int Hq, int d, int block_size, int max_blocks_per_seq);
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
+// The same launch with the library's own per-device scratch array as the
+// workspace (a.workspace is ignored); needs decode_workspace_bytes(...) <=
+// decode_scratch_bytes(), which the caller checks.
+size_t decode_scratch_bytes();
+hipError_t launch_decode_paged_noalloc(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace attn

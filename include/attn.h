@@ -224,6 +224,28 @@ int attn_decode_paged(const void* q, const void* kcache, const void* vcache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_paged without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It allocates nothing and calls no
+ * allocating routine: the partial results live in the library's own device
+ * array of 16 MiB per GPU (set up when the library's code is loaded on that
+ * GPU and kept until the process ends).  The first call on each device looks
+ * up the array's address (a HIP symbol query, no allocation).  Arguments,
+ * layouts and results are those of attn_decode_paged (the same kernels; the
+ * outputs are equal bit for bit); ATTN_E_WORKSPACE when
+ * attn_decode_paged_workspace_size(B, Hq, d, block_size, max_blocks_per_seq)
+ * exceeds 16 MiB (e.g. B <= 16 with Hq * d <= 4096).  Nothing in the array
+ * needs to start at zero.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (different streams or threads) race
+ * and must not be made.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* kcache, const void* vcache,
+                              const int* block_table, const int* seq_lens, void* out,
+                              float* lse, int B, int Hq, int Hkv, int d, int block_size,
+                              int max_blocks_per_seq, int num_blocks, int window, float scale,
+                              void* stream);
+
+/*
  * Bytes of device workspace attn_prefill_paged needs for these sizes (0 when
  * no query tile can need more than one key chunk of 8192 keys, i.e.
  * max_blocks_per_seq * block_size <= 8192; 0 for invalid sizes).  Pure host
