@@ -52,6 +52,7 @@
 //     loads its 8 rows of a key tile from the cache block that holds them.
 #include <atomic>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -148,26 +149,30 @@ __device__ __forceinline__ TileRange tile_range(int i0, int Nq, int Nk, int caus
 }
 
 // Scheduling counters of the persistent kernel: slot s holds one unit counter
-// per XCD.  A counter is a 64-bit word, a launch's tag (high half) and the
-// next unit index (low half).  Every launch has its own tag (a host counter),
-// takes slot tag % kSchedSlots, and is preceded on its stream by a one-wave
-// kernel that sets the slot's counters to (tag, 0), so a launch replayed from
-// a captured graph starts afresh.  A work group claims a unit by
-// compare-and-swap and its claims only increase: it takes the counter's index
-// (or one past its own previous claim, if that is larger), and a counter that
-// carries another launch's tag (another launch in flight on the same slot) is
-// taken over at one past the group's previous claim.  Under this launch's
-// tag the indices handed out always form a prefix [0, max], so no unit is
-// skipped: a group leaves only after claiming an index past its range.
-// Sharing a slot makes launches repeat some units (each unit writes the same
-// values again), nothing more.
+// per XCD, a 64-bit word made of the launch's tag (high half) and the next
+// unit index (low half).  Every launch takes a fresh tag and a slot, and is
+// preceded on its stream by a one-wave kernel that sets the slot's counters
+// to (tag, 0); a work group claims units with one atomic add.  The host makes
+// slot use exclusive: a launch on a slot whose previous launch may still run
+// waits for it (an event recorded after each launch), and a launch captured
+// into a graph gets a slot of its own (see launch()), whose set-up kernel is
+// replayed with it.  Should two launches still meet on one counter (replays
+// of two graphs whose captures are kGraphSlots captures apart, running at
+// the same time), the tag shows it: the group then takes the counter over
+// for its own launch at one past its previous claim (claims only increase,
+// and under one tag the indices handed out stay a prefix [0, max], so the
+// launch skips no unit; the other may, since the add already took an index).
 constexpr int kXcds = 8;  // XCDs of the device; work group w runs on XCD w % 8
-constexpr int kSchedSlotsMax = 1024;
-__device__ unsigned long long g_sched[kSchedSlotsMax * kXcds];
+constexpr int kEagerSlots = 256;  // slots of launches made outside graph capture
+constexpr int kGraphSlots = 4096;  // slots of captured launches, taken in turn
+__device__ unsigned long long g_sched[(kEagerSlots + kGraphSlots) * kXcds];
 
 // Next unit index of this launch from counter `w`; `last` is this group's
 // previous claim (-1 before the first).
 __device__ __forceinline__ int claim_unit(unsigned long long* w, unsigned tag, int last) {
+  const unsigned long long old = atomicAdd(w, 1ull);
+  if ((unsigned)(old >> 32) == tag && (int)(unsigned)old > last) return (int)(unsigned)old;
+  // another launch's tag (or an index at or below ours after a take-over)
   unsigned long long v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const unsigned next = (unsigned)(last + 1);
   for (;;) {
@@ -1015,18 +1020,53 @@ long long fwd_bf16_grid(int B, int Hq, int Nq) {
 
 namespace {
 
-std::atomic<unsigned> g_launches{0};          // tags handed out so far
-std::atomic<int> g_sched_slots{kSchedSlotsMax};  // slots in use (tests may lower it)
+// Host side of the scheduling counters, per device: the tag counter, the
+// next eager and graph slots, and for each eager slot an event recorded after
+// the last launch that used it.
+constexpr int kMaxDevices = 64;
+struct SchedState {
+  std::mutex mu;
+  unsigned tag = 0;
+  int next_eager = 0, next_graph = 0;
+  int eager_slots = kEagerSlots;  // slots in turn (tests may lower it)
+  hipEvent_t ev[kEagerSlots] = {};
+  bool recorded[kEagerSlots] = {};
+};
+SchedState g_state[kMaxDevices];
 
-// one persistent work group per CU (the LDS ring admits one per CU); each
-// launch takes a fresh tag and the slot it names, whose counters a one-wave
-// kernel sets first
+// one persistent work group per CU (the LDS ring admits one per CU)
 template <int MODE>
 hipError_t launch(Params& p, int d, float scale, long long units, hipStream_t stream) {
-  unsigned tag = g_launches.fetch_add(1, std::memory_order_relaxed) + 1u;
-  if (tag == 0) tag = g_launches.fetch_add(1, std::memory_order_relaxed) + 1u;  // 0 is no one's
-  p.tag = tag;
-  p.slot = (int)(tag % (unsigned)g_sched_slots.load(std::memory_order_relaxed));
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return e;
+  SchedState& st = g_state[dev];
+  std::lock_guard<std::mutex> lock(st.mu);
+  if (++st.tag == 0) ++st.tag;  // 0 is no launch's tag
+  p.tag = st.tag;
+  int eager = -1;
+  if (cap != hipStreamCaptureStatusNone) {
+    // a slot of its own: replays of this graph reuse it, set up afresh each time
+    p.slot = kEagerSlots + st.next_graph;
+    st.next_graph = (st.next_graph + 1) % kGraphSlots;
+  } else {
+    eager = st.next_eager % st.eager_slots;
+    st.next_eager = (eager + 1) % st.eager_slots;
+    p.slot = eager;
+    if (st.recorded[eager]) {
+      // the slot's previous launch may still run (on any stream): wait for it
+      e = hipEventQuery(st.ev[eager]);
+      if (e == hipErrorNotReady) e = hipStreamWaitEvent(stream, st.ev[eager], 0);
+      if (e != hipSuccess) return e;
+    } else if (st.ev[eager] == nullptr) {
+      e = hipEventCreateWithFlags(&st.ev[eager], hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+  }
   hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, stream, p.slot, p.tag);
   const int cus = device_cus();
   const dim3 grid(units < cus ? (int)units : cus), block(kThreads);
@@ -1042,14 +1082,23 @@ hipError_t launch(Params& p, int d, float scale, long long units, hipStream_t st
     else
       hipLaunchKernelGGL((fwd_bf16_kernel<64, false, MODE>), grid, block, 0, stream, p);
   }
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess && eager >= 0) {
+    e = hipEventRecord(st.ev[eager], stream);
+    st.recorded[eager] = e == hipSuccess;
+  }
+  return e;
 }
 
 }  // namespace
 
 int set_fwd_sched_slots(int n) {
-  const int prev = g_sched_slots.load();
-  if (n >= 1 && n <= kSchedSlotsMax) g_sched_slots.store(n);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  SchedState& st = g_state[dev];
+  std::lock_guard<std::mutex> lock(st.mu);
+  const int prev = st.eager_slots;
+  if (n >= 1 && n <= kEagerSlots) st.eager_slots = n;
   return prev;
 }
 

@@ -44,8 +44,9 @@ struct FwdVarlenArgs {
 };
 
 hipError_t launch_fwd_bf16_varlen(const FwdVarlenArgs& a, hipStream_t stream);
-// Number of scheduling-counter slots the bf16 forward launches cycle through
-// (1 .. 1024; other values leave it unchanged); returns the previous number.
+// Number of scheduling-counter slots the bf16 forward launches made outside
+// graph capture take in turn on the current device (1 .. 256; other values
+// leave it unchanged); returns the previous number.
 int set_fwd_sched_slots(int n);
 // Work units of the packed launch (for the size check).
 long long fwd_bf16_varlen_grid(int n_seqs, int Hq, int total_q);

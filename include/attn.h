@@ -66,18 +66,20 @@
  *   - `scale` is used as given (callers normally pass 1/sqrt(d)).
  *   - The library is thread-safe.  Its state is a per-device cache of the
  *     compute-unit count, filled on first use, and the scheduling counters of
- *     the bf16 forward kernels (attn_fwd, attn_fwd_varlen, attn_prefill_paged)
- *     in device memory: each launch takes a fresh tag and one of 1024 counter
- *     slots in turn, and is preceded on its stream by a one-wave kernel that
- *     sets that slot to its tag.  Launches in flight on different slots are
- *     independent.  Two launches running at once on the same slot (1024 or
- *     more in flight) still compute their results exactly, but may repeat
- *     work units.
- *   - Graph capture: a forward call records two kernel launches (the counter
- *     set-up and the kernel); the tag is fixed in the captured launch, and
- *     every replay sets its slot afresh, so replays in turn are correct.
- *     Replays of one captured call must not overlap each other (they also
- *     write the same outputs).
+ *     the bf16 forward kernels (attn_fwd, attn_fwd_varlen, attn_prefill_paged):
+ *     each launch takes a fresh tag and a slot of counters in device memory,
+ *     and is preceded on its stream by a one-wave kernel that sets the slot up.
+ *     Slot use is exclusive: 256 slots are taken in turn, and a launch whose
+ *     slot's previous launch has not finished first waits for it on its stream
+ *     (an event the library records after each launch), so any number of
+ *     launches may be in flight on any streams.
+ *   - Graph capture: a forward call made while its stream is capturing
+ *     records two kernel launches (the counter set-up and the kernel) and
+ *     takes a slot of its own, out of 4096 reserved for captured calls and
+ *     reused in turn; no event is recorded.  Every replay sets the slot up
+ *     again, so replays in turn are correct.  Replays of one captured call
+ *     must not overlap each other (they also write the same outputs), nor may
+ *     replays of calls captured 4096 captures apart.
  */
 #ifndef ATTN_MI355X_ATTN_H
 #define ATTN_MI355X_ATTN_H
@@ -342,10 +344,11 @@ const char* attn_status_str(int status);
 
 /*
  * Testing hook: the number of scheduling-counter slots the bf16 forward
- * launches cycle through (1 .. 1024, default 1024; other values leave it
- * unchanged).  Returns the previous number.  Fewer slots make concurrent
- * launches share counters, which exercises the shared-slot path; results
- * do not change.  Host state only; no HIP call.
+ * launches made outside graph capture take in turn on the current device
+ * (1 .. 256, default 256; other values leave it unchanged).  Returns the
+ * previous number (-1 if no device is current).  With one slot, every launch
+ * waits for the previous one, whatever its stream; results do not change.
+ * Host state only; the only HIP call is the current-device query.
  */
 int attn_set_fwd_sched_slots(int n);
 

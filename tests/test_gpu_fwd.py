@@ -256,11 +256,11 @@ def test_persistent_queue_reuse_and_streams():
         assert torch.equal(out, refs[s][0]) and torch.equal(lse, refs[s][1]), f"launch {n} shape {s}"
 
 
-def test_shared_counter_slot_still_exact():
-    """With a single counter slot every launch shares it: one long launch on
-    one stream and 70 short launches of two shapes on another, in flight
-    together, take over each other's counters.  Work may be repeated, but every
-    launch must still reproduce a lone launch bit for bit."""
+def test_single_counter_slot_still_exact():
+    """With a single counter slot every launch reuses the slot of the launch
+    before it: one long launch on one stream and 70 short launches of three
+    shapes on another, enqueued together, must each wait for the slot's
+    previous user and reproduce a lone launch bit for bit."""
     from exact_softmax_attention_amd import _lib
     inputs, refs = _sched_inputs()
     prev = _lib.lib().attn_set_fwd_sched_slots(1)
@@ -283,3 +283,34 @@ def test_shared_counter_slot_still_exact():
     assert torch.equal(long_res[0], refs[0][0]) and torch.equal(long_res[1], refs[0][1])
     for n, (s, (out, lse)) in enumerate(short):
         assert torch.equal(out, refs[s][0]) and torch.equal(lse, refs[s][1]), f"short {n} shape {s}"
+
+
+def test_captured_graph_replays_match_eager():
+    """A forward call captured into a graph (its counter set-up kernel and the
+    kernel, on a slot of its own) replayed several times, with eager launches
+    and synchronisations between the replays, reproduces the eager result bit
+    for bit on every replay."""
+    inputs, refs = _sched_inputs()
+    qd, kd, vd, causal, w = inputs[3]
+    out = torch.empty_like(qd)
+    lse = torch.empty((qd.shape[0], qd.shape[2], qd.shape[1]), dtype=torch.float32,
+                      device=qd.device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        attn_fwd(qd, kd, vd, causal=causal, window=w, out=out, lse=lse)  # warm-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        attn_fwd(qd, kd, vd, causal=causal, window=w, out=out, lse=lse)
+    for rep in range(4):
+        out.zero_()
+        lse.zero_()
+        # eager work on other shapes between the replays
+        o1, l1 = attn_fwd(*inputs[1][:3], causal=inputs[1][3], window=inputs[1][4])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, refs[3][0]) and torch.equal(lse, refs[3][1]), f"replay {rep}"
+        assert torch.equal(o1, refs[1][0]) and torch.equal(l1, refs[1][1])
