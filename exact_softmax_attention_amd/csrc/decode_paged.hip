@@ -175,8 +175,10 @@ __global__ __launch_bounds__(64 * kGroupWaves) void decode_split_kernel(const Pa
     // K as the A operand of S^T = K Q^T and V rows (RPI rows an instruction);
     // two register sets, filled alternately.
     u32x4 kA[T::KC], kB[T::KC], vA[T::VI], vB[T::VI];
-    auto fetch = [&](int i, u32x4 (&rk)[T::KC], u32x4 (&rv)[T::VI]) {
-      int phys = trow[i];
+    // block ids are read two blocks ahead of their fetch (scalar loads whose
+    // latency would otherwise sit in front of every block's K/V loads)
+    auto fetch = [&](int id, u32x4 (&rk)[T::KC], u32x4 (&rv)[T::VI]) {
+      int phys = id;
       if (phys < 0 || phys >= p.num_blocks) {
         bad = true;
         phys = 0;
@@ -190,7 +192,8 @@ __global__ __launch_bounds__(64 * kGroupWaves) void decode_split_kernel(const Pa
       for (int j = 0; j < T::VI; ++j)
         rv[j] = *reinterpret_cast<const u32x4*>(vp + (int64_t)j * T::RPI * row_elems);
     };
-    fetch(0, kA, vA);
+    int id_b = trow[min(1, count - 1)], id_c = trow[min(2, count - 1)];
+    fetch(trow[0], kA, vA);
 
     // Q^T as the B operand: lane (n, g) holds head n, the same features as K
     bf16x8 qf[T::KC];
@@ -276,11 +279,15 @@ __global__ __launch_bounds__(64 * kGroupWaves) void decode_split_kernel(const Pa
     // The prefetch index is clamped, so the last block is read twice (the
     // second time from cache) rather than branching around the loads.
     for (int i = 0; i < count; i += 2) {
-      fetch(min(i + 1, count - 1), kB, vB);
+      // ids of blocks i+3 and i+4 for the next trip; id_b, id_c: blocks i+1, i+2
+      const int id_d = trow[min(i + 3, count - 1)], id_e = trow[min(i + 4, count - 1)];
+      fetch(id_b, kB, vB);
       compute(i, kA, vA);
       if (i + 1 >= count) break;
-      fetch(min(i + 2, count - 1), kA, vA);
+      fetch(id_c, kA, vA);
       compute(i + 1, kB, vB);
+      id_b = id_d;
+      id_c = id_e;
     }
 
     // l over the four lanes of each head; one partial per (wave, sequence)
