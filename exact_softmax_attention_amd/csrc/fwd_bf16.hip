@@ -348,8 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   const int j = per_head - 1 - (unit - bh * per_head);
   for (int e = 0; e < 2; ++e) {
     if (e == 1 && (VARLEN || !p.pairing || j == nq - 1 - j)) break;
-    if (e == 1) __syncthreads();  // the first tile's O staging is done with the ring
-    if (PAGED && tid == 0) s_bad = 0;  // read by the previous item before the barrier above
+    if (PAGED && tid == 0) s_bad = 0;  // read by the previous item before the unit's last barrier
     // this item: query tile qt of head h of sequence b, whose Nq query rows
     // start at token row q_tok0 and Nk key rows at k_tok0
     int b, h, qt, Nq, Nk;
@@ -608,9 +607,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     // M(k): scores of tile k, then P V of tile k-1, as one stream of MFMAs
     // whose LDS fragment reads run LA MFMAs ahead (the V reads start while the
     // score MFMAs still run).  U = k mod S (compile time), so every LDS slot
-    // offset is an immediate.
-    auto m_phase = [&](auto U, int k, int& vcase) __attribute__((always_inline)) {
+    // offset is an immediate.  M(0) (FIRST) has no P V half.
+    auto m_phase = [&](auto U, auto FIRST, int k, int& vcase) __attribute__((always_inline)) {
       constexpr int u = decltype(U)::value;
+      constexpr int NM = decltype(FIRST)::value ? NQK : NQK + NPV;  // MFMAs of this phase
       // case of tile k for the V phase (scalar work, done here where the
       // issue slots are idle): 0 no mask, 1 masked, 2 not visible
       constexpr int ks = u;                // slot of K(k)
@@ -674,18 +674,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       auto read = [&](int j) __attribute__((always_inline)) { if (j < NQK) kread(j); else vread(j - NQK); };
   #pragma unroll
       for (int j = 0; j < NPRE; ++j) kf[j] = kpre[j];
+      static_assert(NQK >= 5, "the loads ride on the score MFMAs");
   #pragma unroll
-      for (int j = 0; j < NQK + NPV; ++j) {
-        if (j + LA < NQK + NPV && j + LA >= NPRE) read(j + LA);
+      for (int j = 0; j < NM; ++j) {
+        if (j + LA < NM && j + LA >= NPRE) read(j + LA);
         if (j < NQK) qk_mfma(j); else pv_mfma(j - NQK);
         if (j < 5) piece(j);
       }
   #pragma unroll
-      for (int j = 0; j < NQK + NPV; ++j) {
+      for (int j = 0; j < NM; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (j + LA < NQK && j + LA >= NPRE)
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        else if (j + LA >= NQK && j + LA < NQK + NPV)
+        else if (j + LA >= NQK && j + LA < NM)
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       if (!group_b) wait_vm<2 * T::LPW * (S - 2)>();
@@ -802,11 +803,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       if (group_b) wait_vm<2 * T::LPW * (S - 3)>();
     };
 
-    // prologue: K(0..S-2) and V(0..S-3) in LDS before the first barrier; the
-    // slot of "V(-1)", which M(0) multiplies by zero probabilities, is zeroed
-    // (stale LDS could hold NaN)
-    for (int i = tid; i < T::TILEB / 16; i += kThreads)
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + (2 * S - 1) * T::TILEB + 16 * i) = u32x4{};
+    // prologue: K(0..S-2) and V(0..S-3) in LDS before the first barrier
     unrolled_while<0, S - 1>([&](auto T_) { issue_k(T_); return true; });
     unrolled_while<0, S - 2>([&](auto T_) { issue_v(T_); return true; });
     if constexpr (PAGED) {  // M(0) loads K tile S-1 and V tile S-2
@@ -821,19 +818,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     if (group_b) lds_barrier();  // B starts one slot behind A
   #pragma unroll
     for (int j = 0; j < NPRE; ++j) kpre[j] = kfrag(0, j);
-    // S tiles per trip so that every LDS slot index is a compile-time constant;
-    // the last step (k = n_tiles) only finishes P V of the last tile
-    for (int k0 = 0;; k0 += S) {
-      const bool more = unrolled_while<0, S>([&](auto U) {
-        const int k = k0 + decltype(U)::value;
-        int vcase;
-        m_phase(U, k, vcase);
-        lds_barrier();
-        v_phase(U, k, vcase);
-        lds_barrier_reads_in_flight();
-        return k < n_tiles;
-      });
-      if (!more) break;
+    auto step = [&](auto U, auto FIRST, int k) __attribute__((always_inline)) {
+      int vcase;
+      m_phase(U, FIRST, k, vcase);
+      lds_barrier();
+      v_phase(U, k, vcase);
+      lds_barrier_reads_in_flight();
+      return k < n_tiles;
+    };
+    // M(0) has no P V half (there is no tile before tile 0); then S tiles per
+    // trip from k = 1, so that every LDS slot index is a compile-time
+    // constant; the last step (k = n_tiles) only finishes P V of the last tile
+    if (step(integral_constant<int, 0>{}, std::true_type{}, 0)) {
+      for (int k0 = 1;; k0 += S) {
+        const bool more = unrolled_while<0, S>([&](auto I) {
+          constexpr int u = (decltype(I)::value + 1) % S;
+          return step(integral_constant<int, u>{}, std::false_type{}, k0 + decltype(I)::value);
+        });
+        if (!more) break;
+      }
     }
     if (!group_b) lds_barrier();  // A's extra barrier matches B's first one
     wait_vm<0>();  // loads past the last tile still land in LDS: drain them
@@ -842,11 +845,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     __syncthreads();
     if constexpr (PAGED) bad = s_bad != 0;
 
-    // epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2.  O goes
-    // through this wave's own LDS region (the ring is idle now), so that it
-    // leaves as whole 256-byte rows (16 lanes x 16 bytes) rather than as
-    // 8-byte pieces scattered over 32 rows.  The row pitch of 2D + 16 bytes
-    // spreads the scattered writes over the banks.
+    // epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
     float la = l_run, lb = l_run;
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(la), "+v"(lb));
     const float l_tot = la + lb;
@@ -873,39 +872,50 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
                              : l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
       }
     } else {
-    constexpr int OPITCH = T::ROWB + 16;  // bytes per staged row
-    static_assert(kWaves * kRowsPerWave * OPITCH <= T::LDS_BYTES, "O staging fits the ring");
-    const uint32_t ostage = wave * kRowsPerWave * OPITCH;
+      // O leaves through LDS as whole rows (rather than as 8-byte pieces
+      // scattered over 32 rows), feature half by feature half, in the slots
+      // that the next item's prologue does not load: K slot S-1 (waves 0-3)
+      // and V slot S-1 (waves 4-7), 32 rows x D/2 features per wave.  The
+      // next item's first barrier comes before its M(0) loads K slot S-1.
+      // The 16-byte pieces of a staged half row are XOR-swizzled by (row / RB)
+      // so that a write of all 64 lanes spreads over the 64 banks.
+      constexpr int HB = T::ROWB / 2;     // bytes of a half row
+      constexpr int HP = HB / 16;         // its 16-byte pieces
+      constexpr int RB = 256 / HB;        // half rows per 256 bytes (all banks)
+      constexpr int RPI = 64 / HP;        // half rows per read instruction
+      static_assert(kWaves / 2 * kRowsPerWave * HB == T::TILEB, "a slot stages four waves");
+      const uint32_t sbase = ((group_b ? S : 0) + S - 1) * T::TILEB +
+                             (wave & (kWaves / 2 - 1)) * kRowsPerWave * HB;
+      const int rr = lane / HP, cc = lane % HP;
   #pragma unroll
-    for (int db = 0; db < T::NDB; ++db)
+      for (int half = 0; half < 2; ++half) {
   #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = db * 32 + r4 * 8 + g * 4;
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[db][r4 * 4 + 0] * inv, acc[db][r4 * 4 + 1] * inv);
-        w[1] = pack_bf16x2(acc[db][r4 * 4 + 2] * inv, acc[db][r4 * 4 + 3] * inv);
-        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds + ostage + n * OPITCH + 2 * d) = w;
+        for (int dl = 0; dl < T::NDB / 2; ++dl)
+  #pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int db = half * (T::NDB / 2) + dl;
+            const int piece = (dl * 4 + r4) ^ ((n / RB) & (HP - 1));
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[db][r4 * 4 + 0] * inv, acc[db][r4 * 4 + 1] * inv);
+            w[1] = pack_bf16x2(acc[db][r4 * 4 + 2] * inv, acc[db][r4 * 4 + 3] * inv);
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds + sbase + n * HB + piece * 16 + g * 8) = w;
+          }
+        // this wave's own region: its LDS accesses complete in order
+  #pragma unroll
+        for (int i = 0; i < kRowsPerWave / RPI; ++i) {
+          const int r = i * RPI + rr;
+          const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+              lds + sbase + r * HB + ((cc ^ ((r / RB) & (HP - 1))) * 16));
+          if (qw0 + r < Nq)
+            *reinterpret_cast<u32x4*>(p.o + (q_tok0 + qw0 + r) * q_row + (int64_t)h * D + half * (D / 2) + 8 * cc) = w;
+        }
       }
-    {
-      constexpr int LPR = T::ROWB / 16;     // lanes per row
-      constexpr int RPI = 64 / LPR;         // rows per store instruction
-      const int rr = lane / LPR, cc = lane % LPR;
-  #pragma unroll
-      for (int i = 0; i < kRowsPerWave / RPI; ++i) {
-        const int r = i * RPI + rr;
-        const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-            lds + ostage + r * OPITCH + 16 * cc);
-        if (qw0 + r < Nq)
-          *reinterpret_cast<u32x4*>(p.o + (q_tok0 + qw0 + r) * q_row + (int64_t)h * D + 8 * cc) = w;
-      }
-    }
-    const int row = qw0 + n;
-    if (row < Nq && p.lse != nullptr && g == 0)
-      p.lse[lse0 + row] = (PAGED && bad) ? __builtin_nanf("")
-                          : l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+      const int row = qw0 + n;
+      if (row < Nq && p.lse != nullptr && g == 0)
+        p.lse[lse0 + row] = (PAGED && bad) ? __builtin_nanf("")
+                            : l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
     }
   }
-  // the O staging is done with the ring before the next unit's loads
   if (tid == 0) s_unit = first + grabbed;
   __syncthreads();
   unit = s_unit;
