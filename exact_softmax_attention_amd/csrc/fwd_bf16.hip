@@ -377,6 +377,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
         const int len = p.seq_lens[b];
         bad = len < 0 || len > p.max_blocks * kBlockTokens;
         Nk = bad ? 0 : len;
+        // A block id outside the pool anywhere in the sequence's table makes
+        // the whole sequence NaN, as a bad length does: every item of the
+        // sequence finds it here, whichever blocks the item itself reads (the
+        // tile and chunk split is kept, so the merge pass sees NaN partials).
+        // The ids are checked again where blocks are read.
+        if (!bad) {
+          const int nblk = (len + kBlockTokens - 1) / kBlockTokens;
+          const int* const ids = p.table + (int64_t)b * p.max_blocks;
+          bool out = false;
+          for (int i = lane; i < nblk; i += 64) out |= (unsigned)ids[i] >= (unsigned)p.num_blocks;
+          bad = __builtin_amdgcn_ballot_w64(out) != 0;
+        }
       } else {
         k0 = clampi(p.cu_k[b], 0, p.total_k);
         Nk = clampi(p.cu_k[b + 1], k0, p.total_k) - k0;
@@ -818,10 +830,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     if (group_b) lds_barrier();  // B starts one slot behind A
   #pragma unroll
     for (int j = 0; j < NPRE; ++j) kpre[j] = kfrag(0, j);
+    // The matrix phase runs at a raised wave priority: the vector phase of
+    // the other wave on the SIMD (the older one, for group B) otherwise wins
+    // the issue arbitration over its MFMAs.
     auto step = [&](auto U, auto FIRST, int k) __attribute__((always_inline)) {
       int vcase;
+      __builtin_amdgcn_s_setprio(1);
       m_phase(U, FIRST, k, vcase);
       lds_barrier();
+      __builtin_amdgcn_s_setprio(0);
       v_phase(U, k, vcase);
       lds_barrier_reads_in_flight();
       return k < n_tiles;

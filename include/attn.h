@@ -285,11 +285,11 @@ size_t attn_prefill_paged_workspace_size(int num_seqs, int total_q, int Hq, int 
  * + i and sees the cached tokens up to it (the last `window` of them when
  * window > 0).  Rows at negative positions (nq_s > seq_lens[s]) see no key
  * and get O = 0, LSE = -inf.  A sequence whose length is negative or exceeds
- * max_blocks_per_seq * block_size gets NaN in all its rows; a block id
- * outside [0, num_blocks) that a 256-row query tile needs gets NaN in that
- * tile's rows (a sequence of at most 256 new tokens without a window: all
- * of them).  Nothing outside the pool, the used table entries and the given
- * rows is read; rows of q outside every sequence are not written.  The cu
+ * max_blocks_per_seq * block_size, or whose table names a block outside
+ * [0, num_blocks) among its first ceil(seq_lens[s] / block_size) entries
+ * (read or not), gets NaN in all its rows.  Nothing outside the pool, those
+ * table entries and the given rows is read; rows of q outside every
+ * sequence are not written.  The cu
  * array follows the rules of attn_fwd_varlen.
  *
  * block_size must be 16; d in {64, 128}; Hq % Hkv == 0; num_seqs *

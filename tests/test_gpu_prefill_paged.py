@@ -149,6 +149,34 @@ def test_bad_block_id_and_bad_length_give_nan():
     check(out[cu[0]:cu[1]], O[cu[0]:cu[1]], lse[:, cu[0]:cu[1]], L[:, cu[0]:cu[1]], "bf16", "seq 0")
 
 
+def test_bad_block_id_makes_the_whole_sequence_nan():
+    """A block id outside the pool gives NaN in every row of its sequence, as in
+    the oracle, also where the bad block is read by only one of several query
+    tiles, by only one of two key chunks, or by none (before the window)."""
+    # sequence 0: 600 new tokens (3 query tiles), block 55 (keys 880..895) is
+    # not seen by the rows at positions 400..655; sequence 1: 9000 keys (two
+    # chunks of 8192), block 10 lies in the first chunk only; sequence 2 clean
+    lens, chunks = [1000, 9000, 300], [600, 300, 100]
+    inp = _make(lens, chunks, 2, 1, 128, 3350)
+    nbk = inp["kcache"].shape[0]
+    inp["block_table"][0, 55] = nbk
+    inp["block_table"][1, 10] = -3
+    out, lse = _run(inp, 0.1, 0)
+    O, L = _oracle(inp, 0.1, 0)
+    cu = inp["cu_seqlens_q"].tolist()
+    assert np.isnan(O[cu[0]:cu[2]]).all() and np.isnan(L[:, cu[0]:cu[2]]).all()
+    assert torch.isnan(out[cu[0]:cu[2]].float()).all()
+    assert torch.isnan(lse[:, cu[0]:cu[2]]).all()
+    check(out[cu[2]:cu[3]], O[cu[2]:cu[3]], lse[:, cu[2]:cu[3]], L[:, cu[2]:cu[3]], "bf16", "seq 2")
+    # window 256 over 3000 keys: block 5 (keys 80..95) is before every row's window
+    inp = _make([3000], [50], 2, 2, 64, 3351)
+    inp["block_table"][0, 5] = inp["kcache"].shape[0] + 1
+    out, lse = _run(inp, 0.1, 256)
+    O, L = _oracle(inp, 0.1, 256)
+    assert np.isnan(O).all() and np.isnan(L).all()
+    assert torch.isnan(out.float()).all() and torch.isnan(lse).all()
+
+
 def test_deterministic():
     inp = _make([900, 1500], [300, 700], 8, 2, 128, 3400)
     a = _run(inp, 0.088, 0)
