@@ -34,9 +34,10 @@
 //                dQ^T += K^T dS^T              A = K^T from the transposing load
 //              so P, D and the log-sum-exp are one value per lane.
 // Tiles go through registers into LDS (double-buffered: the next tile's
-// global loads are in flight while the current one is computed).  Rows are
-// padded to a pitch of 2D + 16 bytes, which keeps both the row reads and the
-// transposing reads of the same tile free of most bank conflicts.
+// global loads are in flight while the current one is computed).  The
+// 16-byte pieces of a staged row are XOR-swizzled (BT::swz), which keeps both
+// the row reads and the transposing reads of the same tile free of bank
+// conflicts.
 #include <type_traits>
 
 #include "device_common.h"
@@ -131,7 +132,20 @@ template <int D>
 struct BT {
   static constexpr int KC = D / 16;            // k-chunks over the head dimension
   static constexpr int NDB = D / 32;           // 32-feature blocks of dK^T, dV^T, dQ^T
-  static constexpr int PITCH = 2 * D + 16;     // LDS bytes per staged row
+  static constexpr int PITCH = 2 * D;          // LDS bytes per staged row (no padding)
+  // 16-byte piece swizzle (XOR on the piece index) of a staged row.  The LDS
+  // serves 256 bytes (its 64 banks) at a time: 16 lanes of a 16-byte row read
+  // or 32 lanes of an 8-byte transposing read.  Row reads take one piece of
+  // 16 consecutive rows, so the swizzle must differ on each of them; the
+  // transposing reads take 64 bytes (4 pieces) of 4 consecutive rows, which
+  // the swizzle must move to 4 different quarters of the 256 bytes.  D = 128
+  // (a row is 256 bytes): bits 2-3 follow row % 4, bits 0-1 row / 4 % 4.
+  // D = 64 (two rows per 256 bytes): bit 2 follows row / 2 % 2, bits 0-1
+  // row / 4 % 4.
+  __device__ static int swz(int row) {
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                    : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  }
   static constexpr int ROWB = 2 * D;           // global bytes per row
   static constexpr int PIECES = ROWB / 16;     // 16-byte pieces per row
 };
@@ -177,16 +191,18 @@ struct Stage {
     for (int i = 0; i < NP; ++i) {
       const int p = tid + i * kBwdThreads;
       const int row = p / BT<D>::PIECES, pc = p % BT<D>::PIECES;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + off + row * BT<D>::PITCH + pc * 16) = r[i];
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          lds + off + row * BT<D>::PITCH + ((pc ^ BT<D>::swz(row)) << 4)) = r[i];
     }
   }
 };
 
 // A operand (rows x k) of a 32x32x16 MFMA from a staged tile: lane l reads row
-// row0 + l % 32, features 16c + 8 (l / 32) .. +7.
+// l % 32, features 16c + 8 (l / 32) .. +7 (piece 2c + l / 32 of the row).
 template <int D>
 __device__ __forceinline__ bf16x8 row_frag(const lds_u8* lds, uint32_t off, int lane, int c) {
-  const uint32_t a = off + (lane & 31) * BT<D>::PITCH + (16 * c + 8 * (lane >> 5)) * 2;
+  const int row = lane & 31;
+  const uint32_t a = off + row * BT<D>::PITCH + (((2 * c + (lane >> 5)) ^ BT<D>::swz(row)) << 4);
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
 }
 
@@ -199,10 +215,13 @@ template <int D>
 __device__ __forceinline__ bf16x8 tr_frag(const lds_u8* lds, uint32_t off, int lane, int db, int kc) {
   const int G16 = lane >> 4, s16 = lane & 15;
   const int row = kc * 16 + (G16 >> 1) * 4 + (s16 >> 2);
-  const int feat = db * 32 + 16 * (G16 & 1) + 4 * (s16 & 3);
-  const uint32_t a = off + row * BT<D>::PITCH + feat * 2;
+  // features 32 db + 16 (G16 % 2) + 4 (s16 % 4): piece 4 db + 2 (G16 % 2) +
+  // (s16 % 4) / 2, byte 8 (s16 % 2) within it; the second read is 8 rows on
+  const int piece = 4 * db + 2 * (G16 & 1) + ((s16 & 3) >> 1);
+  const uint32_t a = off + row * BT<D>::PITCH + ((piece ^ BT<D>::swz(row)) << 4) + 8 * (s16 & 1);
+  const uint32_t b = off + (row + 8) * BT<D>::PITCH + ((piece ^ BT<D>::swz(row + 8)) << 4) + 8 * (s16 & 1);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + a + 8 * BT<D>::PITCH));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + b));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
