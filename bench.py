@@ -115,10 +115,12 @@ def parse():
     ap.add_argument("--skip-prefill-paged", action="store_true")
     ap.add_argument("--skip-dense-extra", action="store_true",
                     help="leave out the GQA/MQA 16K and sliding-window 32K objects")
-    ap.add_argument("--mode", choices=["bench", "copy", "stream"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "copy", "stream", "ceiling"], default="bench",
                     help="copy: a plain device copy of known size (counter calibration); "
                          "stream: a contiguous read of the decode workload's byte count "
-                         "(the memory system's rate for a plain streaming read)")
+                         "(the memory system's rate for a plain streaming read); "
+                         "ceiling: the read_ceiling program (contiguous, random-block and "
+                         "per-KV-head-slice reads of the decode workload's bytes)")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic.json from rocprofv3 --pmc runs under DIR "
                          "(no GPU needed)")
@@ -307,6 +309,24 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
 
+    if args.mode == "ceiling":
+        # a program of its own (built with the library), run as a child process
+        import subprocess
+        from exact_softmax_attention_amd.build import CEILING_BIN
+        if not os.path.exists(CEILING_BIN):
+            print(f"bench.py: {CEILING_BIN} is missing: run the build first", file=sys.stderr)
+            sys.exit(1)
+        out = subprocess.run([CEILING_BIN], capture_output=True, text=True)
+        if out.returncode != 0:
+            print(out.stderr, file=sys.stderr)
+            sys.exit(out.returncode)
+        res = json.loads(out.stdout.strip().splitlines()[-1])
+        res = {"mode": "ceiling", **res,
+               "of_peak": {k: round(v / metrics.PEAK_HBM_GBS, 4) for k, v in res.items()
+                           if k.endswith("GBps")}}
+        print(json.dumps(res))
+        return
+
     if args.mode == "copy":
         n = COPY_BYTES
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -456,7 +476,13 @@ def main():
                                "gradients of the materialised definition"),
                            "roofline": {"bound": "mfma", "achieved": round(btf, 2),
                                         "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                        "frac": round(btf / metrics.PEAK_BF16_TFLOPS, 4)}}
+                                        "frac": round(btf / metrics.PEAK_BF16_TFLOPS, 4)},
+                           # what the kernels execute: dK/dV recomputes S and dP, and dQ
+                           # recomputes them again (seven products, 3.5x the forward)
+                           "executed": {"flop_per_call": metrics.bwd_executed_flops(
+                               cfg.B, cfg.Hq, cfg.Nq, cfg.Nk, cfg.d, cfg.causal, cfg.window),
+                               "TFLOP/s": round(btf * 3.5 / 2.5, 2),
+                               "frac": round(btf * 3.5 / 2.5 / metrics.PEAK_BF16_TFLOPS, 4)}}
     if not args.skip_varlen and args.workload is None:
         print(f"bench: varlen {PACKED}", file=sys.stderr, flush=True)
         from exact_softmax_attention_amd import attn_fwd_varlen

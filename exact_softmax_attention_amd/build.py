@@ -99,7 +99,24 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_read_ceiling()
     return LIB
+
+
+# The decode's read-bandwidth ceiling probe: a program of its own (not part of
+# the library), run by `bench.py --mode ceiling`.
+CEILING_SRC = os.path.join(CSRC, "read_ceiling.hip")
+CEILING_BIN = os.path.join(PKG, "read_ceiling")
+
+
+def build_read_ceiling() -> str:
+    tmp = CEILING_BIN + ".tmp"
+    cmd = [hipcc()] + common_flags() + ["-o", tmp, CEILING_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling read_ceiling failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    os.replace(tmp, CEILING_BIN)
+    return CEILING_BIN
 
 
 if __name__ == "__main__":

@@ -59,6 +59,14 @@ def bwd_flops(B: int, Hq: int, Nq: int, Nk: int, d: int, causal: bool, window: i
     return 2.5 * fwd_flops(B, Hq, Nq, Nk, d, causal, window)
 
 
+def bwd_executed_flops(B: int, Hq: int, Nq: int, Nk: int, d: int, causal: bool,
+                       window: int) -> float:
+    """Flops the backward kernels execute on the visible pairs: the dK/dV pass
+    forms S, dP, dV and dK, the dQ pass S, dP and dQ again: seven products the
+    size of the forward's two, 3.5x forward."""
+    return 3.5 * fwd_flops(B, Hq, Nq, Nk, d, causal, window)
+
+
 def fwd_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, elt: int = 2,
               with_lse: bool = True) -> int:
     qo = 2 * B * Nq * Hq * d * elt
