@@ -58,6 +58,45 @@ def test_shards_merged_equal_full_attention(case):
     check(out, O[:, q0:], lse, L[:, :, q0:], "bf16", str(case))
 
 
+# Ring attention over 8 or 16 devices: the running result is kept in bf16 and
+# merged in place once per shard, so each merge adds one bf16 rounding of O.
+MANY = [
+    # B, N, Hq, Hkv, d, shards (equal; the last holds the queries), causal
+    (1, 4096, 4, 2, 128, 8, True),
+    (1, 2048, 2, 1, 64, 16, False),
+]
+
+
+@pytest.mark.parametrize("case", MANY, ids=lambda c: f"N{c[1]}_h{c[2]}x{c[3]}_d{c[4]}_s{c[5]}_{'c' if c[6] else 'n'}")
+def test_many_shards_merged_in_place(case):
+    """8 and 16 shards merged into one running bf16 result stay within the
+    fp64 oracle's tolerance, and the rounding added by the merges stays within
+    a few times that of one launch over all keys."""
+    B, N, Hq, Hkv, d, S, causal = case
+    seed = 5300 + MANY.index(case)
+    print(f"case {case} seed {seed}", flush=True)
+    q, k, v = workloads.make_dense(B, Hq, Hkv, N, N, d, seed)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    bounds = [N * i // S for i in range(S + 1)]
+    out, lse = _shard_attention(q, k, v, bounds, causal, scale)
+    q0 = bounds[-2]
+    res = oracle.attention(q, k, v, scale, causal, 0,
+                           heads=[(b, h) for b in range(B) for h in range(Hq)],
+                           rows=np.arange(q0, N))
+    O = np.zeros((B, N - q0, Hq, d))
+    L = np.zeros((B, Hq, N - q0))
+    for (b, h), (o, l) in res.items():
+        O[b, :, h] = o
+        L[b, h] = l
+    _, merged_mean, _ = check(out, O, lse, L, "bf16", f"{S} shards")
+    # one launch over all keys, for the same rows
+    o1, l1 = attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    _, one_mean, _ = check(o1.cpu()[:, q0:], O, l1.cpu()[:, :, q0:], L, "bf16", "one launch")
+    print(f"mean-abs error: {S} shards merged {merged_mean:.3e}, one launch {one_mean:.3e}")
+    assert merged_mean <= 4 * one_mean + 1e-6
+
+
 def test_merge_with_an_empty_side_is_exact():
     # a partial over no keys (O = 0, LSE = -inf) leaves the other side unchanged
     B, N, H, d = 2, 100, 4, 128
