@@ -266,50 +266,52 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV.
 
+constexpr int kDkdvWaves = 8;  // 4 producer waves + 4 consumer waves
+constexpr int kDkdvThreads = kDkdvWaves * 64;
+
+// One work group per (128-key tile, KV head, batch), 8 waves in two roles
+// sharing the tile's keys (wave w and w + 4 own keys 32 (w % 4) .. +31 and
+// run on one SIMD):
+//   producer (waves 0-3) holds its keys' K and V rows as B operands and, for
+//     query block s, forms S = Q K^T and dP = dO V^T, then P and dS = P (dP - D),
+//     which it leaves in LDS as the bf16 B operands of the consumer's products;
+//   consumer (waves 4-7) holds the dK^T and dV^T accumulators and, for block
+//     s - 1, adds dO^T P and Q^T dS (A: the transposed tiles from LDS); it also
+//     stages the Q and dO tiles (through registers, kAhead blocks ahead).
+// Each wave fits half a SIMD's registers, so the two roles' MFMAs, softmax
+// and loads overlap on the SIMD.  Per iteration s: producers work on block s
+// (tile buffer s % 3, probability buffer s % 2), consumers on block s - 1 and
+// store block s + 1 into tile buffer (s + 1) % 3 (last read in iteration
+// s - 1); one barrier per iteration.
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams p) {
   using T = BT<D>;
-  constexpr int QTILE = T::PITCH * kBlk;  // bytes of one staged 32-row tile
-  // [buffer][Q, dO] tiles, then [buffer][lse2, D] (32 floats each)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * QTILE + 2 * 2 * kBlk * 4];
+  constexpr int QTILE = T::PITCH * kBlk;     // bytes of one staged 32-row tile
+  constexpr int kTB = 3;                     // tile buffers (Q, dO, lse2, D)
+  constexpr int TBUF = 2 * QTILE + 2 * kBlk * 4;
+  constexpr int PW = 2 * 2 * 64 * 16;        // one wave's P and dS operands: [kc][P, dS][lane] x 16 bytes
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kTB * TBUF + 2 * 4 * PW];
   lds_u8* const lds = (lds_u8*)smem;
-  const uint32_t stat0 = 4 * QTILE;
+  constexpr uint32_t pbuf0 = kTB * TBUF;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave < 4;
+  const int kw = wave & 3;                       // key block of this wave
   const SeqTile sq = seq_tile<VARLEN>(p, p.cu_k, p.total_k, lane);
   if (sq.tile < 0) return;  // a schedule slot past the sequence (whole group)
   const int Nq = sq.Nq, Nk = sq.Nk;
   const int kt = sq.tile, hk = blockIdx.y;
-  const int k0 = kt * kBwdWaves * kBlk;          // first key of the tile
-  const int kw0 = k0 + wave * kBlk;              // first key of this wave
+  const int k0 = kt * 4 * kBlk;                  // first key of the tile
+  const int kw0 = k0 + kw * kBlk;                // first key of this wave's block
   const int key = kw0 + (lane & 31);             // this lane's key (column)
   const int g = lane >> 5;
   const int delta = Nk - Nq;
   const int64_t kv_row = (int64_t)p.Hkv * D;
   const int64_t q_row = (int64_t)p.Hq * D;
 
-  // K and V of the lane's key as B operands (features 16c + 8g .. +7)
-  bf16x8 kb[T::KC], vb[T::KC];
-  {
-    const int64_t off = (sq.k0 + key) * kv_row + (int64_t)hk * D + 8 * g;
-#pragma unroll
-    for (int c = 0; c < T::KC; ++c) {
-      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (key < Nk) {
-        x = *reinterpret_cast<const u32x4*>(p.k + off + 16 * c);
-        y = *reinterpret_cast<const u32x4*>(p.v + off + 16 * c);
-      }
-      kb[c] = __builtin_bit_cast(bf16x8, x);
-      vb[c] = __builtin_bit_cast(bf16x8, y);
-    }
-  }
-  f32x16 dkt[T::NDB], dvt[T::NDB];
-#pragma unroll
-  for (int db = 0; db < T::NDB; ++db) dkt[db] = dvt[db] = f32x16{};
-
   // query rows that see some key of the tile: [qlo, qhi)
-  const int klast = min(Nk, k0 + kBwdWaves * kBlk) - 1;
+  const int klast = min(Nk, k0 + 4 * kBlk) - 1;
   int qlo = 0, qhi = Nq;
   if (p.causal) qlo = max(0, k0 - delta);
   if (p.window > 0) qhi = min(Nq, klast - delta + p.window);
@@ -317,14 +319,110 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
   const int q_first = qlo & ~(kBlk - 1);
   const int steps = nblk * p.group;  // (head, block) pairs, head-major
 
-  // step t's tiles travel in register set t % kAhead: loaded kAhead steps
-  // before they are computed, stored to LDS buffer t % 2 one step before
+  // does this wave's 32 x 32 block of step s hold any visible pair, and does it need a mask?
+  auto block_case = [&](int s, bool& any, bool& full) __attribute__((always_inline)) {
+    const int i0 = q_first + (s % nblk) * kBlk;
+    any = kw0 < Nk;
+    if (p.causal && kw0 > i0 + kBlk - 1 + delta) any = false;
+    if (p.window > 0 && i0 + delta - (kw0 + kBlk - 1) >= p.window) any = false;
+    full = (!p.causal || kw0 + kBlk - 1 <= i0 + delta) &&
+           (p.window <= 0 || i0 + kBlk - 1 + delta - kw0 < p.window);
+  };
+  auto pb = [&](int s, int kc, int which) __attribute__((always_inline)) {
+    return pbuf0 + (uint32_t)(s & 1) * 4 * PW + kw * PW + (uint32_t)((kc * 2 + which) * 64 + lane) * 16;
+  };
+
+  if (producer) {
+    // K and V of the lane's key as B operands (features 16c + 8g .. +7)
+    bf16x8 kb[T::KC], vb[T::KC];
+    {
+      const int64_t off = (sq.k0 + key) * kv_row + (int64_t)hk * D + 8 * g;
+#pragma unroll
+      for (int c = 0; c < T::KC; ++c) {
+        u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+        if (key < Nk) {
+          x = *reinterpret_cast<const u32x4*>(p.k + off + 16 * c);
+          y = *reinterpret_cast<const u32x4*>(p.v + off + 16 * c);
+        }
+        kb[c] = __builtin_bit_cast(bf16x8, x);
+        vb[c] = __builtin_bit_cast(bf16x8, y);
+      }
+    }
+    __syncthreads();  // the consumers' first tile is in LDS
+    for (int s = 0; s <= steps; ++s) {
+      if (s < steps) {
+        bool any, full;
+        block_case(s, any, full);
+        if (any) {
+          const int i0 = q_first + (s % nblk) * kBlk;
+          const int b = s % kTB;
+          const uint32_t qoff = b * TBUF, ooff = qoff + QTILE;
+          const uint32_t loff = qoff + 2 * QTILE, doff = loff + kBlk * 4;
+          // S = Q K^T and dP = dO V^T (lane: key, 16 rows)
+          f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+          for (int c = 0; c < T::KC; ++c) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, qoff, lane, c), kb[c], sacc, 0, 0, 0);
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, ooff, lane, c), vb[c], dpacc, 0, 0, 0);
+          }
+          float pr[16], ds[16];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            // rows 4g + 8t .. +3 of the block: their lse2 and D
+            const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + loff + (4 * g + 8 * t) * 4);
+            const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + doff + (4 * g + 8 * t) * 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pr[4 * t + u] = fast_exp2(sacc[4 * t + u] * p.sl2 - l4[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ds[4 * t + u] = dpacc[4 * t + u] - d4[u];
+          }
+          if (!full) {
+            // register r holds row i0 + 4g + c(r), c(r) = r % 4 + 8 (r / 4); with
+            // t = key - (i0 + 4g + delta): hidden by causality when t > c(r), by the
+            // window when t <= c(r) - window
+            const int tk = key - (i0 + 4 * g + delta);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int c = (r & 3) + 8 * (r >> 2);
+              bool hide = p.causal && tk > c;
+              if (p.window > 0 && tk <= c - p.window) hide = true;
+              if (hide) pr[r] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ds[r] *= pr[r];
+          // P and dS as the consumer's B operands, one 16-byte piece per lane
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+            u32x4 pp, pd;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pp[i] = pack_bf16x2(pr[8 * kc + 2 * i], pr[8 * kc + 2 * i + 1]);
+              pd[i] = pack_bf16x2(ds[8 * kc + 2 * i], ds[8 * kc + 2 * i + 1]);
+            }
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + pb(s, kc, 0)) = pp;
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + pb(s, kc, 1)) = pd;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // consumer: stages the tiles (thread ct of 256) and accumulates dK^T, dV^T
+  const int ct = tid - 4 * 64;
+  f32x16 dkt[T::NDB], dvt[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) dkt[db] = dvt[db] = f32x16{};
+  // step t's tiles travel in register set t % kAhead, loaded kAhead steps
+  // before they are stored, and sit in tile buffer t % 3
   struct Set {
     Stage<D, kBlk> q, o;
-    float l2, d;  // lse2 and D of row tid (tid < 32)
+    float l2, d;  // lse2 and D of row ct (ct < 32)
   };
   Set sets[kAhead];
-  const StageOff<D, kBlk> so(q_row, tid);
+  const StageOff<D, kBlk> so(q_row, ct);
   auto fetch = [&](Set& st, int s) __attribute__((always_inline)) {
     if (s >= steps) return;
     const int h = hk * p.group + s / nblk;
@@ -333,97 +431,55 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams p
     const uint16_t* ob = p.dout + sq.q0 * q_row + (int64_t)h * D;
     st.q.load(qb, q_row, i0, Nq, so);
     st.o.load(ob, q_row, i0, Nq, so);
-    if (tid < kBlk) {
-      const int i = i0 + tid;
+    if (ct < kBlk) {
+      const int i = i0 + ct;
       const int64_t o = sq.stat(p, h, VARLEN) + i;
       st.l2 = i < Nq ? p.lse2[o] : __builtin_inff();
       st.d = i < Nq ? p.dsum[o] : 0.f;
     }
   };
-  auto stash = [&](const Set& st, int buf) __attribute__((always_inline)) {
-    st.q.store(lds, (2 * buf) * QTILE, tid);
-    st.o.store(lds, (2 * buf + 1) * QTILE, tid);
-    if (tid < kBlk) {
-      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + stat0 + (2 * buf) * kBlk * 4 + tid * 4) = st.l2;
-      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + stat0 + (2 * buf + 1) * kBlk * 4 + tid * 4) = st.d;
+  auto stash = [&](const Set& st, int b) __attribute__((always_inline)) {
+    st.q.store(lds, b * TBUF, ct);
+    st.o.store(lds, b * TBUF + QTILE, ct);
+    if (ct < kBlk) {
+      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + b * TBUF + 2 * QTILE + ct * 4) = st.l2;
+      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + b * TBUF + 2 * QTILE + kBlk * 4 + ct * 4) = st.d;
     }
   };
-
+  static_assert(kAhead == kTB, "one register set and one tile buffer per step modulo 3");
   unroll_while<0, kAhead>([&](auto J) { fetch(sets[J], J); return true; });
   if (steps > 0) {
     stash(sets[0], 0);
     fetch(sets[0], kAhead);
   }
   __syncthreads();
-  for (int s0 = 0; s0 < steps; s0 += kAhead) {
+  for (int s0 = 0; s0 <= steps; s0 += kAhead) {
    const bool more = unroll_while<0, kAhead>([&](auto U) __attribute__((always_inline)) {
-    constexpr int u = decltype(U)::value;
+    constexpr int u = decltype(U)::value;  // s % 3
     const int s = s0 + u;
-    if (s >= steps) return false;
-    const int buf = s & 1;
-    const int i0 = q_first + (s % nblk) * kBlk;
-    const uint32_t qoff = (2 * buf) * QTILE, ooff = (2 * buf + 1) * QTILE;
-    const uint32_t loff = stat0 + (2 * buf) * kBlk * 4, doff = stat0 + (2 * buf + 1) * kBlk * 4;
-    // does this wave's 32 x 32 block hold any visible pair, and does it need a mask?
-    bool any = kw0 < Nk;
-    if (p.causal && kw0 > i0 + kBlk - 1 + delta) any = false;
-    if (p.window > 0 && i0 + delta - (kw0 + kBlk - 1) >= p.window) any = false;
-    const bool full = (!p.causal || kw0 + kBlk - 1 <= i0 + delta) &&
-                      (p.window <= 0 || i0 + kBlk - 1 + delta - kw0 < p.window);
-    if (any) {
-      // S = Q K^T and dP = dO V^T (lane: key, 16 rows)
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    if (s > steps) return false;
+    if (s >= 1) {
+      // dV^T += dO^T P and dK^T += Q^T dS of block s - 1
+      bool any, full;
+      block_case(s - 1, any, full);
+      if (any) {
+        constexpr int bp = (u + kTB - 1) % kTB;  // tile buffer of block s - 1
+        const uint32_t qoff = bp * TBUF, ooff = qoff + QTILE;
 #pragma unroll
-      for (int c = 0; c < T::KC; ++c) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, qoff, lane, c), kb[c], sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, ooff, lane, c), vb[c], dpacc, 0, 0, 0);
-      }
-      float pr[16], ds[16];
+        for (int kc = 0; kc < 2; ++kc) {
+          const bf16x8 bpv = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + pb(s - 1, kc, 0));
+          const bf16x8 bdv = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + pb(s - 1, kc, 1));
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        // rows 4g + 8t .. +3 of the block: their lse2 and D
-        const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + loff + (4 * g + 8 * t) * 4);
-        const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + doff + (4 * g + 8 * t) * 4);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) pr[4 * t + u] = fast_exp2(sacc[4 * t + u] * p.sl2 - l4[u]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ds[4 * t + u] = dpacc[4 * t + u] - d4[u];
-      }
-      if (!full) {
-        // register r holds row i0 + 4g + c(r), c(r) = r % 4 + 8 (r / 4); with
-        // t = key - (i0 + 4g + delta): hidden by causality when t > c(r), by the
-        // window when t <= c(r) - window
-        const int tk = key - (i0 + 4 * g + delta);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = (r & 3) + 8 * (r >> 2);
-          bool hide = p.causal && tk > c;
-          if (p.window > 0 && tk <= c - p.window) hide = true;
-          if (hide) pr[r] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ds[r] *= pr[r];
-      // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-row chunks
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        u32x4 pp, pd;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pp[i] = pack_bf16x2(pr[8 * kc + 2 * i], pr[8 * kc + 2 * i + 1]);
-          pd[i] = pack_bf16x2(ds[8 * kc + 2 * i], ds[8 * kc + 2 * i + 1]);
-        }
-        const bf16x8 bp = __builtin_bit_cast(bf16x8, pp), bd = __builtin_bit_cast(bf16x8, pd);
-#pragma unroll
-        for (int db = 0; db < T::NDB; ++db) {
-          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, ooff, lane, db, kc), bp, dvt[db], 0, 0, 0);
-          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, qoff, lane, db, kc), bd, dkt[db], 0, 0, 0);
+          for (int db = 0; db < T::NDB; ++db) {
+            dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, ooff, lane, db, kc), bpv, dvt[db], 0, 0, 0);
+            dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, qoff, lane, db, kc), bdv, dkt[db], 0, 0, 0);
+          }
         }
       }
     }
-    // the other buffer's readers (step s - 1) passed the previous barrier
+    // block s + 1 into tile buffer (s + 1) % 3, last read in iteration s - 1
     if (s + 1 < steps) {
-      stash(sets[(u + 1) % kAhead], buf ^ 1);
+      stash(sets[(u + 1) % kAhead], (u + 1) % kTB);
       fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
     }
     __syncthreads();
@@ -640,9 +696,9 @@ hipError_t launch_bwd(const BwdParams& p, int d, long long rows, dim3 g1, dim3 g
   }
   if ((long long)g1.x * g1.y * g1.z > 0) {
     if (d == 128)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, VARLEN>), g1, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, VARLEN>), g1, dim3(kDkdvThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<64, VARLEN>), g1, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, VARLEN>), g1, dim3(kDkdvThreads), 0, stream, p);
   }
   if ((long long)g2.x * g2.y * g2.z > 0) {
     if (d == 128)
