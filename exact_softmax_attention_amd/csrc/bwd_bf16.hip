@@ -511,143 +511,191 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
 // ---------------------------------------------------------------------------
 // dQ.
 
+// One work group per 128-row query tile of one head, 8 waves in the two roles
+// of the dK/dV kernel (wave w and w + 4 own rows 32 (w % 4) .. +31):
+//   producer (waves 0-3) holds its rows' Q and dO as B operands and, for key
+//     step s (two 32-key blocks), forms S^T = K Q^T and dP^T = V dO^T, then
+//     dS^T, which it leaves in LDS as bf16 B operands;
+//   consumer (waves 4-7) holds the dQ^T accumulators, adds K^T dS^T of step
+//     s - 1 (A: the transposed K tile from LDS) and stages the K/V tiles.
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p) {
   using T = BT<D>;
   constexpr int KN = 64;                  // keys per step (two 32-key blocks)
   constexpr int KTILE = T::PITCH * KN;    // bytes of one staged K or V tile
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * KTILE];
+  constexpr int kTB = 3;                  // tile buffers
+  constexpr int PW = 2 * 2 * 64 * 16;     // one wave's dS^T operands: [block][kc][lane] x 16 bytes
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kTB * 2 * KTILE + 2 * 4 * PW];
   lds_u8* const lds = (lds_u8*)smem;
+  constexpr uint32_t pbuf0 = kTB * 2 * KTILE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave < 4;
+  const int rw = wave & 3;                 // row block of this wave
   const SeqTile sq = seq_tile<VARLEN>(p, p.cu_q, p.total_q, lane);
   if (sq.tile < 0) return;  // a schedule slot past the sequence (whole group)
   const int Nq = sq.Nq, Nk = sq.Nk;
   const int qt = sq.tile, h = blockIdx.y;
   const int hk = h / p.group;
-  const int q0 = qt * kBwdWaves * kBlk;
-  const int qw0 = q0 + wave * kBlk;
+  const int q0 = qt * 4 * kBlk;
+  const int qw0 = q0 + rw * kBlk;
   const int row = qw0 + (lane & 31);       // this lane's query row (column of S^T)
   const int g = lane >> 5;
   const int delta = Nk - Nq;
   const int64_t kv_row = (int64_t)p.Hkv * D;
   const int64_t q_row = (int64_t)p.Hq * D;
 
-  bf16x8 qb[T::KC], ob[T::KC];
-  float l2 = __builtin_inff(), dd = 0.f;
-  {
-    const int64_t off = (sq.q0 + row) * q_row + (int64_t)h * D + 8 * g;
-#pragma unroll
-    for (int c = 0; c < T::KC; ++c) {
-      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (row < Nq) {
-        x = *reinterpret_cast<const u32x4*>(p.q + off + 16 * c);
-        y = *reinterpret_cast<const u32x4*>(p.dout + off + 16 * c);
-      }
-      qb[c] = __builtin_bit_cast(bf16x8, x);
-      ob[c] = __builtin_bit_cast(bf16x8, y);
-    }
-    if (row < Nq) {
-      const int64_t o = sq.stat(p, h, VARLEN) + row;
-      l2 = p.lse2[o];
-      dd = p.dsum[o];
-    }
-  }
-  f32x16 dqt[T::NDB];
-#pragma unroll
-  for (int db = 0; db < T::NDB; ++db) dqt[db] = f32x16{};
-
   // keys some row of the tile sees: [jlo, jhi)
-  const int qlast = min(Nq, q0 + kBwdWaves * kBlk) - 1;
+  const int qlast = min(Nq, q0 + 4 * kBlk) - 1;
   int jlo = 0, jhi = Nk;
   if (p.causal) jhi = min(Nk, qlast + delta + 1);
   if (p.window > 0) jlo = max(0, q0 + delta - p.window + 1);
   const int j_first = jlo & ~(KN - 1);
   const int steps = jhi > j_first ? (jhi - j_first + KN - 1) / KN : 0;
 
-  // as in the dK/dV kernel: step t's K and V tiles travel in register set
-  // t % kAhead and LDS buffer t % 2
+  // does this wave's 32 x 32 block (key block kb2 of step s) hold any visible pair / need a mask?
+  auto block_case = [&](int s, int kb2, bool& any, bool& full) __attribute__((always_inline)) {
+    const int jb = j_first + s * KN + kb2 * kBlk;
+    any = qw0 < Nq && jb < Nk;
+    if (p.causal && jb > qw0 + kBlk - 1 + delta) any = false;
+    if (p.window > 0 && qw0 + delta - (jb + kBlk - 1) >= p.window) any = false;
+    full = (!p.causal || jb + kBlk - 1 <= qw0 + delta) &&
+           (p.window <= 0 || qw0 + kBlk - 1 + delta - jb < p.window);
+  };
+  auto pb = [&](int s, int kb2, int kc) __attribute__((always_inline)) {
+    return pbuf0 + (uint32_t)(s & 1) * 4 * PW + rw * PW + (uint32_t)((kb2 * 2 + kc) * 64 + lane) * 16;
+  };
+
+  if (producer) {
+    bf16x8 qb[T::KC], ob[T::KC];
+    float l2 = __builtin_inff(), dd = 0.f;
+    {
+      const int64_t off = (sq.q0 + row) * q_row + (int64_t)h * D + 8 * g;
+#pragma unroll
+      for (int c = 0; c < T::KC; ++c) {
+        u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+        if (row < Nq) {
+          x = *reinterpret_cast<const u32x4*>(p.q + off + 16 * c);
+          y = *reinterpret_cast<const u32x4*>(p.dout + off + 16 * c);
+        }
+        qb[c] = __builtin_bit_cast(bf16x8, x);
+        ob[c] = __builtin_bit_cast(bf16x8, y);
+      }
+      if (row < Nq) {
+        const int64_t o = sq.stat(p, h, VARLEN) + row;
+        l2 = p.lse2[o];
+        dd = p.dsum[o];
+      }
+    }
+    __syncthreads();  // the consumers' first tiles are in LDS
+    for (int s = 0; s <= steps; ++s) {
+      if (s < steps) {
+        const int b = s % kTB;
+        const uint32_t koff = (2 * b) * KTILE, voff = (2 * b + 1) * KTILE;
+#pragma unroll
+        for (int kb2 = 0; kb2 < KN / kBlk; ++kb2) {
+          bool any, full;
+          block_case(s, kb2, any, full);
+          if (!any) continue;
+          const int jb = j_first + s * KN + kb2 * kBlk;
+          const uint32_t kb_off = koff + kb2 * kBlk * T::PITCH, vb_off = voff + kb2 * kBlk * T::PITCH;
+          // S^T = K Q^T, dP^T = V dO^T (lane: row, 16 keys)
+          f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+          for (int c = 0; c < T::KC; ++c) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, kb_off, lane, c), qb[c], sacc, 0, 0, 0);
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, vb_off, lane, c), ob[c], dpacc, 0, 0, 0);
+          }
+          float pr[16], ds[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(sacc[r] * p.sl2 - l2);
+          if (!full) {
+            // register r holds key jb + 4g + c(r); with t = jb + 4g - (row + delta)
+            // the key is past the row's position when t + c(r) > 0 and before its
+            // window when t + c(r) <= -window
+            const int tk = jb + 4 * g - (row + delta);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int c = (r & 3) + 8 * (r >> 2);
+              bool hide = p.causal && tk + c > 0;
+              if (p.window > 0 && tk + c <= -p.window) hide = true;
+              if (hide) pr[r] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dpacc[r] - dd);
+          // dS^T as the consumer's B operands (the block's two 16-key chunks)
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+            u32x4 pd;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pd[i] = pack_bf16x2(ds[8 * kc + 2 * i], ds[8 * kc + 2 * i + 1]);
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + pb(s, kb2, kc)) = pd;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // consumer: stages the K/V tiles (thread ct of 256) and accumulates dQ^T
+  const int ct = tid - 4 * 64;
+  f32x16 dqt[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) dqt[db] = f32x16{};
+  // step t's K and V tiles travel in register set t % kAhead and sit in tile buffer t % 3
   struct Set {
     Stage<D, KN> k, v;
   };
   Set sets[kAhead];
   const uint16_t* kbase = p.k + sq.k0 * kv_row + (int64_t)hk * D;
   const uint16_t* vbase = p.v + sq.k0 * kv_row + (int64_t)hk * D;
-  const StageOff<D, KN> so(kv_row, tid);
+  const StageOff<D, KN> so(kv_row, ct);
   auto fetch = [&](Set& st, int s) __attribute__((always_inline)) {
     if (s >= steps) return;
     st.k.load(kbase, kv_row, j_first + s * KN, Nk, so);
     st.v.load(vbase, kv_row, j_first + s * KN, Nk, so);
   };
-  auto stash = [&](const Set& st, int buf) __attribute__((always_inline)) {
-    st.k.store(lds, (2 * buf) * KTILE, tid);
-    st.v.store(lds, (2 * buf + 1) * KTILE, tid);
+  auto stash = [&](const Set& st, int b) __attribute__((always_inline)) {
+    st.k.store(lds, (2 * b) * KTILE, ct);
+    st.v.store(lds, (2 * b + 1) * KTILE, ct);
   };
+  static_assert(kAhead == kTB, "one register set and one tile buffer per step modulo 3");
   unroll_while<0, kAhead>([&](auto J) { fetch(sets[J], J); return true; });
   if (steps > 0) {
     stash(sets[0], 0);
     fetch(sets[0], kAhead);
   }
   __syncthreads();
-  for (int s0 = 0; s0 < steps; s0 += kAhead) {
+  for (int s0 = 0; s0 <= steps; s0 += kAhead) {
    const bool more = unroll_while<0, kAhead>([&](auto U) __attribute__((always_inline)) {
-    constexpr int u = decltype(U)::value;
+    constexpr int u = decltype(U)::value;  // s % 3
     const int s = s0 + u;
-    if (s >= steps) return false;
-    const int buf = s & 1;
-    const int j0 = j_first + s * KN;
-    const uint32_t koff = (2 * buf) * KTILE, voff = (2 * buf + 1) * KTILE;
+    if (s > steps) return false;
+    if (s >= 1) {
+      constexpr int bp = (u + kTB - 1) % kTB;  // tile buffer of step s - 1
+      const uint32_t koff = (2 * bp) * KTILE;
 #pragma unroll
-    for (int kb2 = 0; kb2 < KN / kBlk; ++kb2) {
-      const int jb = j0 + kb2 * kBlk;  // first key of the 32-key block
-      bool any = qw0 < Nq && jb < Nk;
-      if (p.causal && jb > qw0 + kBlk - 1 + delta) any = false;
-      if (p.window > 0 && qw0 + delta - (jb + kBlk - 1) >= p.window) any = false;
-      const bool full = (!p.causal || jb + kBlk - 1 <= qw0 + delta) &&
-                        (p.window <= 0 || qw0 + kBlk - 1 + delta - jb < p.window);
-      if (!any) continue;
-      const uint32_t kb_off = koff + kb2 * kBlk * T::PITCH, vb_off = voff + kb2 * kBlk * T::PITCH;
-      // S^T = K Q^T, dP^T = V dO^T (lane: row, 16 keys)
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      for (int kb2 = 0; kb2 < KN / kBlk; ++kb2) {
+        bool any, full;
+        block_case(s - 1, kb2, any, full);
+        if (!any) continue;
+        const uint32_t kb_off = koff + kb2 * kBlk * T::PITCH;
+        // dQ^T += K^T dS^T over the block's two 16-key chunks
 #pragma unroll
-      for (int c = 0; c < T::KC; ++c) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, kb_off, lane, c), qb[c], sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, vb_off, lane, c), ob[c], dpacc, 0, 0, 0);
-      }
-      float pr[16], ds[16];
+        for (int kc = 0; kc < 2; ++kc) {
+          const bf16x8 bd = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + pb(s - 1, kb2, kc));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(sacc[r] * p.sl2 - l2);
-      if (!full) {
-        // register r holds key jb + 4g + c(r); with t = jb + 4g - (row + delta)
-        // the key is past the row's position when t + c(r) > 0 and before its
-        // window when t + c(r) <= -window
-        const int tk = jb + 4 * g - (row + delta);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = (r & 3) + 8 * (r >> 2);
-          bool hide = p.causal && tk + c > 0;
-          if (p.window > 0 && tk + c <= -p.window) hide = true;
-          if (hide) pr[r] = 0.f;
+          for (int db = 0; db < T::NDB; ++db)
+            dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, kb_off, lane, db, kc), bd, dqt[db], 0, 0, 0);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dpacc[r] - dd);
-      // dQ^T += K^T dS^T over the block's two 16-key chunks
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        u32x4 pd;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pd[i] = pack_bf16x2(ds[8 * kc + 2 * i], ds[8 * kc + 2 * i + 1]);
-        const bf16x8 bd = __builtin_bit_cast(bf16x8, pd);
-#pragma unroll
-        for (int db = 0; db < T::NDB; ++db)
-          dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, kb_off, lane, db, kc), bd, dqt[db], 0, 0, 0);
-      }
     }
-    // the other buffer's readers (block s - 1) passed the previous barrier
+    // step s + 1 into tile buffer (s + 1) % 3, last read in iteration s - 1
     if (s + 1 < steps) {
-      stash(sets[(u + 1) % kAhead], buf ^ 1);
+      stash(sets[(u + 1) % kAhead], (u + 1) % kTB);
       fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
     }
     __syncthreads();
@@ -702,9 +750,9 @@ hipError_t launch_bwd(const BwdParams& p, int d, long long rows, dim3 g1, dim3 g
   }
   if ((long long)g2.x * g2.y * g2.z > 0) {
     if (d == 128)
-      hipLaunchKernelGGL((bwd_dq_kernel<128, VARLEN>), g2, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<128, VARLEN>), g2, dim3(kDkdvThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<64, VARLEN>), g2, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<64, VARLEN>), g2, dim3(kDkdvThreads), 0, stream, p);
   }
   return hipGetLastError();
 }
