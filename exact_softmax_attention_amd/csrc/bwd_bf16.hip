@@ -87,10 +87,33 @@ struct BwdParams {
   int n_seqs, total_q, total_k;
 };
 
-// The sequence and 128-row tile of a work group.  Dense: sequence blockIdx.z,
-// tile blockIdx.x.  Packed: blockIdx.x is a slot of the packed axis (queries
-// or keys, `cu` and `total`), the slots of sequence s starting at
-// cu[s] / 128 + s; tile < 0 for a slot past the sequence's tiles.
+// The grid position (x tile or slot, y head, z sequence) a work group works
+// on.  The launch's ids are remapped with xcd_remap, so that each XCD runs one
+// contiguous run of (x, y, z) in order: the tiles of a head then run side by
+// side on one XCD and share its L2 for the rows they all stream (Q, dO and
+// the row statistics for dK/dV; K and V for dQ).  `reverse` takes a head's
+// tiles last to first (dQ: under a causal mask the last query tiles see the
+// most keys, and the longest work should start first).
+struct Wg {
+  int x, y, z;
+};
+
+__device__ __forceinline__ Wg wg_coords(bool reverse) {
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int pid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int m = xcd_remap(pid, gx * gy * (int)gridDim.z);
+  Wg w;
+  w.x = m % gx;
+  w.y = (m / gx) % gy;
+  w.z = m / (gx * gy);
+  if (reverse) w.x = gx - 1 - w.x;
+  return w;
+}
+
+// The sequence and 128-row tile of work group `w`.  Dense: sequence w.z, tile
+// w.x.  Packed: w.x is a slot of the packed axis (queries or keys, `cu` and
+// `total`), the slots of sequence s starting at cu[s] / 128 + s; tile < 0 for
+// a slot past the sequence's tiles.
 struct SeqTile {
   int b, tile, Nq, Nk;
   int64_t q0, k0;  // first query and key row of the sequence
@@ -100,12 +123,12 @@ struct SeqTile {
 };
 
 template <bool VARLEN>
-__device__ __forceinline__ SeqTile seq_tile(const BwdParams& p, const int* cu, int total,
-                                            int lane) {
+__device__ __forceinline__ SeqTile seq_tile(const BwdParams& p, const Wg& w, const int* cu,
+                                            int total, int lane) {
   SeqTile t;
   if constexpr (VARLEN) {
     constexpr int TILE = kBwdWaves * kBlk;
-    const int slot = blockIdx.x;
+    const int slot = w.x;
     t.b = find_seq<TILE>(cu, p.n_seqs, total, slot, lane);
     const int q0 = clampi(p.cu_q[t.b], 0, p.total_q);
     const int k0 = clampi(p.cu_k[t.b], 0, p.total_k);
@@ -118,8 +141,8 @@ __device__ __forceinline__ SeqTile seq_tile(const BwdParams& p, const int* cu, i
     const int off = slot - (a0 / TILE + t.b);
     t.tile = (off >= 0 && off * TILE < len) ? off : -1;
   } else {
-    t.b = blockIdx.z;
-    t.tile = blockIdx.x;
+    t.b = w.z;
+    t.tile = w.x;
     t.Nq = p.Nq;
     t.Nk = p.Nk;
     t.q0 = (int64_t)t.b * p.Nq;
@@ -298,10 +321,11 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = wave < 4;
   const int kw = wave & 3;                       // key block of this wave
-  const SeqTile sq = seq_tile<VARLEN>(p, p.cu_k, p.total_k, lane);
+  const Wg wg = wg_coords(false);
+  const SeqTile sq = seq_tile<VARLEN>(p, wg, p.cu_k, p.total_k, lane);
   if (sq.tile < 0) return;  // a schedule slot past the sequence (whole group)
   const int Nq = sq.Nq, Nk = sq.Nk;
-  const int kt = sq.tile, hk = blockIdx.y;
+  const int kt = sq.tile, hk = wg.y;
   const int k0 = kt * 4 * kBlk;                  // first key of the tile
   const int kw0 = k0 + kw * kBlk;                // first key of this wave's block
   const int key = kw0 + (lane & 31);             // this lane's key (column)
@@ -533,10 +557,11 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = wave < 4;
   const int rw = wave & 3;                 // row block of this wave
-  const SeqTile sq = seq_tile<VARLEN>(p, p.cu_q, p.total_q, lane);
+  const Wg wg = wg_coords(true);
+  const SeqTile sq = seq_tile<VARLEN>(p, wg, p.cu_q, p.total_q, lane);
   if (sq.tile < 0) return;  // a schedule slot past the sequence (whole group)
   const int Nq = sq.Nq, Nk = sq.Nk;
-  const int qt = sq.tile, h = blockIdx.y;
+  const int qt = sq.tile, h = wg.y;
   const int hk = h / p.group;
   const int q0 = qt * 4 * kBlk;
   const int qw0 = q0 + rw * kBlk;
@@ -733,6 +758,10 @@ namespace {
 template <bool VARLEN>
 hipError_t launch_bwd(const BwdParams& p, int d, long long rows, dim3 g1, dim3 g2,
                       hipStream_t stream) {
+  // the work-group remap indexes the grid with 32-bit ints
+  constexpr long long kMaxGroups = 0x7fffffffLL;
+  if ((long long)g1.x * g1.y * g1.z > kMaxGroups || (long long)g2.x * g2.y * g2.z > kMaxGroups)
+    return hipErrorInvalidConfiguration;
   const int rpb = 256 / (d / 8);
   const long long nb = (rows + rpb - 1) / rpb;
   const dim3 g0((unsigned)(nb < 65536 ? nb : 65536));
