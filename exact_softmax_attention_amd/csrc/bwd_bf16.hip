@@ -482,6 +482,13 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
     constexpr int u = decltype(U)::value;  // s % 3
     const int s = s0 + u;
     if (s > steps) return false;
+    // block s + 1 into tile buffer (s + 1) % 3, last read in iteration s - 1;
+    // done first, so that the products below run on the matrix cores while
+    // the producer computes its softmax
+    if (s + 1 < steps) {
+      stash(sets[(u + 1) % kAhead], (u + 1) % kTB);
+      fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
+    }
     if (s >= 1) {
       // dV^T += dO^T P and dK^T += Q^T dS of block s - 1
       bool any, full;
@@ -500,11 +507,6 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
           }
         }
       }
-    }
-    // block s + 1 into tile buffer (s + 1) % 3, last read in iteration s - 1
-    if (s + 1 < steps) {
-      stash(sets[(u + 1) % kAhead], (u + 1) % kTB);
-      fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
     }
     __syncthreads();
     return true;
@@ -699,6 +701,13 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
     constexpr int u = decltype(U)::value;  // s % 3
     const int s = s0 + u;
     if (s > steps) return false;
+    // step s + 1 into tile buffer (s + 1) % 3, last read in iteration s - 1;
+    // done first, so that the products below run on the matrix cores while
+    // the producer computes its softmax
+    if (s + 1 < steps) {
+      stash(sets[(u + 1) % kAhead], (u + 1) % kTB);
+      fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
+    }
     if (s >= 1) {
       constexpr int bp = (u + kTB - 1) % kTB;  // tile buffer of step s - 1
       const uint32_t koff = (2 * bp) * KTILE;
@@ -717,11 +726,6 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
             dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, kb_off, lane, db, kc), bd, dqt[db], 0, 0, 0);
         }
       }
-    }
-    // step s + 1 into tile buffer (s + 1) % 3, last read in iteration s - 1
-    if (s + 1 < steps) {
-      stash(sets[(u + 1) % kAhead], (u + 1) % kTB);
-      fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
     }
     __syncthreads();
     return true;
