@@ -199,10 +199,12 @@ template <int D, int ROWS>
 struct Stage {
   static constexpr int NP = StageOff<D, ROWS>::NP;
   u32x4 r[NP];
+  // on = false: a zero-size range, which reads nothing and gives zeros (the
+  // callers issue the same loads every step, see the consumers' fetch)
   __device__ __forceinline__ void load(const uint16_t* base, int64_t row_stride, int r0, int n_rows,
-                                       const StageOff<D, ROWS>& so) {
-    const int real = min(ROWS, n_rows - r0);  // rows of the block that exist (>= 1)
-    const int bytes = (int)((real - 1) * row_stride * 2) + 2 * D;
+                                       const StageOff<D, ROWS>& so, bool on) {
+    const int real = min(ROWS, n_rows - r0);  // rows of the block that exist (>= 1 if on)
+    const int bytes = on ? (int)((real - 1) * row_stride * 2) + 2 * D : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(base + (int64_t)r0 * row_stride), (short)0, bytes, 0x00020000);
 #pragma unroll
@@ -382,13 +384,23 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
           const int b = s % kTB;
           const uint32_t qoff = b * TBUF, ooff = qoff + QTILE;
           const uint32_t loff = qoff + 2 * QTILE, doff = loff + kBlk * 4;
-          // S = Q K^T and dP = dO V^T (lane: key, 16 rows)
+          // S = Q K^T and dP = dO V^T (lane: key, 16 rows).  All of the
+          // block's operand reads go out before the first product, so that
+          // the products wait for the LDS once rather than once each.
+          bf16x8 qa[T::KC], oa[T::KC];
+#pragma unroll
+          for (int c = 0; c < T::KC; ++c) {
+            qa[c] = row_frag<D>(lds, qoff, lane, c);
+            oa[c] = row_frag<D>(lds, ooff, lane, c);
+          }
           f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
           for (int c = 0; c < T::KC; ++c) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, qoff, lane, c), kb[c], sacc, 0, 0, 0);
-            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, ooff, lane, c), vb[c], dpacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c], kb[c], sacc, 0, 0, 0);
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[c], vb[c], dpacc, 0, 0, 0);
           }
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::KC, 0);  // the reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::KC, 0);  // then the products
           float pr[16], ds[16];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
@@ -447,35 +459,45 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
   };
   Set sets[kAhead];
   const StageOff<D, kBlk> so(q_row, ct);
+  // Every call issues the same loads, whatever the step (a step past the
+  // last reads zero-size ranges, which touch no memory): with a fixed count
+  // of loads per step the compiler waits, before storing a set, only for
+  // that set's loads, not for the two sets fetched after it.  The row
+  // statistics are loaded by every lane (lanes past the block's rows load
+  // its first row again) through ranges that end with row Nq - 1.
   auto fetch = [&](Set& st, int s) __attribute__((always_inline)) {
-    if (s >= steps) return;
-    const int h = hk * p.group + s / nblk;
-    const int i0 = q_first + (s % nblk) * kBlk;
+    const bool on = s < steps;
+    const int sc = on ? s : 0;
+    const int h = hk * p.group + sc / nblk;
+    const int i0 = q_first + (sc % nblk) * kBlk;
     const uint16_t* qb = p.q + sq.q0 * q_row + (int64_t)h * D;
     const uint16_t* ob = p.dout + sq.q0 * q_row + (int64_t)h * D;
-    st.q.load(qb, q_row, i0, Nq, so);
-    st.o.load(ob, q_row, i0, Nq, so);
-    if (ct < kBlk) {
-      const int i = i0 + ct;
-      const int64_t o = sq.stat(p, h, VARLEN) + i;
-      st.l2 = i < Nq ? p.lse2[o] : __builtin_inff();
-      st.d = i < Nq ? p.dsum[o] : 0.f;
-    }
+    st.q.load(qb, q_row, i0, Nq, so, on);
+    st.o.load(ob, q_row, i0, Nq, so, on);
+    const int64_t o0 = sq.stat(p, h, VARLEN) + i0;
+    const int sb = on ? min(kBlk, Nq - i0) * 4 : 0;
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(p.lse2 + o0, (short)0, sb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(p.dsum + o0, (short)0, sb, 0x00020000);
+    const int r = (ct < kBlk ? ct : 0) * 4;
+    st.l2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, r, 0, 0));
+    st.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, r, 0, 0));
   };
-  auto stash = [&](const Set& st, int b) __attribute__((always_inline)) {
+  // the set of step s into tile buffer b; rows past Nq get lse2 = +inf, D = 0
+  auto stash = [&](const Set& st, int b, int s) __attribute__((always_inline)) {
     st.q.store(lds, b * TBUF, ct);
     st.o.store(lds, b * TBUF + QTILE, ct);
     if (ct < kBlk) {
-      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + b * TBUF + 2 * QTILE + ct * 4) = st.l2;
-      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + b * TBUF + 2 * QTILE + kBlk * 4 + ct * 4) = st.d;
+      const bool row = q_first + (s % nblk) * kBlk + ct < Nq;
+      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + b * TBUF + 2 * QTILE + ct * 4) =
+          row ? st.l2 : __builtin_inff();
+      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + b * TBUF + 2 * QTILE + kBlk * 4 + ct * 4) =
+          row ? st.d : 0.f;
     }
   };
   static_assert(kAhead == kTB, "one register set and one tile buffer per step modulo 3");
   unroll_while<0, kAhead>([&](auto J) { fetch(sets[J], J); return true; });
-  if (steps > 0) {
-    stash(sets[0], 0);
-    fetch(sets[0], kAhead);
-  }
+  if (steps > 0) stash(sets[0], 0, 0);
+  fetch(sets[0], kAhead);
   __syncthreads();
   for (int s0 = 0; s0 <= steps; s0 += kAhead) {
    const bool more = unroll_while<0, kAhead>([&](auto U) __attribute__((always_inline)) {
@@ -485,10 +507,8 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
     // block s + 1 into tile buffer (s + 1) % 3, last read in iteration s - 1;
     // done first, so that the products below run on the matrix cores while
     // the producer computes its softmax
-    if (s + 1 < steps) {
-      stash(sets[(u + 1) % kAhead], (u + 1) % kTB);
-      fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
-    }
+    if (s + 1 < steps) stash(sets[(u + 1) % kAhead], (u + 1) % kTB, s + 1);
+    fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
     if (s >= 1) {
       // dV^T += dO^T P and dK^T += Q^T dS of block s - 1
       bool any, full;
@@ -514,6 +534,8 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
    if (!more) break;
   }
 
+  // the loads past the last step (zero-size ranges) have landed before the wave ends
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds key `key`, features
   // 32 db + 8 t + 4 g .. +3 in registers 4 t .. 4 t + 3.
   if (key < Nk) {
@@ -627,13 +649,22 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
           if (!any) continue;
           const int jb = j_first + s * KN + kb2 * kBlk;
           const uint32_t kb_off = koff + kb2 * kBlk * T::PITCH, vb_off = voff + kb2 * kBlk * T::PITCH;
-          // S^T = K Q^T, dP^T = V dO^T (lane: row, 16 keys)
+          // S^T = K Q^T, dP^T = V dO^T (lane: row, 16 keys), the operand reads
+          // first as in the dK/dV kernel
+          bf16x8 ka[T::KC], va[T::KC];
+#pragma unroll
+          for (int c = 0; c < T::KC; ++c) {
+            ka[c] = row_frag<D>(lds, kb_off, lane, c);
+            va[c] = row_frag<D>(lds, vb_off, lane, c);
+          }
           f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
           for (int c = 0; c < T::KC; ++c) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, kb_off, lane, c), qb[c], sacc, 0, 0, 0);
-            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(lds, vb_off, lane, c), ob[c], dpacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qb[c], sacc, 0, 0, 0);
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c], ob[c], dpacc, 0, 0, 0);
           }
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::KC, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::KC, 0);
           float pr[16], ds[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(sacc[r] * p.sl2 - l2);
@@ -680,10 +711,13 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
   const uint16_t* kbase = p.k + sq.k0 * kv_row + (int64_t)hk * D;
   const uint16_t* vbase = p.v + sq.k0 * kv_row + (int64_t)hk * D;
   const StageOff<D, KN> so(kv_row, ct);
+  // the same loads every step, as in the dK/dV kernel (a step past the last
+  // reads zero-size ranges)
   auto fetch = [&](Set& st, int s) __attribute__((always_inline)) {
-    if (s >= steps) return;
-    st.k.load(kbase, kv_row, j_first + s * KN, Nk, so);
-    st.v.load(vbase, kv_row, j_first + s * KN, Nk, so);
+    const bool on = s < steps;
+    const int j0 = j_first + (on ? s : 0) * KN;
+    st.k.load(kbase, kv_row, j0, Nk, so, on);
+    st.v.load(vbase, kv_row, j0, Nk, so, on);
   };
   auto stash = [&](const Set& st, int b) __attribute__((always_inline)) {
     st.k.store(lds, (2 * b) * KTILE, ct);
@@ -691,10 +725,8 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
   };
   static_assert(kAhead == kTB, "one register set and one tile buffer per step modulo 3");
   unroll_while<0, kAhead>([&](auto J) { fetch(sets[J], J); return true; });
-  if (steps > 0) {
-    stash(sets[0], 0);
-    fetch(sets[0], kAhead);
-  }
+  if (steps > 0) stash(sets[0], 0);
+  fetch(sets[0], kAhead);
   __syncthreads();
   for (int s0 = 0; s0 <= steps; s0 += kAhead) {
    const bool more = unroll_while<0, kAhead>([&](auto U) __attribute__((always_inline)) {
@@ -704,10 +736,8 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
     // step s + 1 into tile buffer (s + 1) % 3, last read in iteration s - 1;
     // done first, so that the products below run on the matrix cores while
     // the producer computes its softmax
-    if (s + 1 < steps) {
-      stash(sets[(u + 1) % kAhead], (u + 1) % kTB);
-      fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
-    }
+    if (s + 1 < steps) stash(sets[(u + 1) % kAhead], (u + 1) % kTB);
+    fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
     if (s >= 1) {
       constexpr int bp = (u + kTB - 1) % kTB;  // tile buffer of step s - 1
       const uint32_t koff = (2 * bp) * KTILE;
@@ -733,6 +763,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
    if (!more) break;
   }
 
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loads past the last step have landed
   if (row < Nq) {
     const int64_t off = (sq.q0 + row) * q_row + (int64_t)h * D;
 #pragma unroll
