@@ -49,6 +49,41 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for raw 32-bit addressing: loads at byte offsets >= bytes
+// return zero and touch no memory.
+__device__ __forceinline__ i32x4 dma_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(a));
+  r[1] = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu);
+  r[2] = static_cast<int>(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Loads that write LDS directly: 16 (dma16) or 4 (dma4) bytes per active
+// lane from the buffer at byte offset voffset to LDS address lds + 16 x lane
+// (4 x lane).  The compiler does not see them: the kernel waits for them
+// itself (wait_vm) before the barrier that hands the data to other waves.
+// M0 (the LDS address of the load) is set inside the asm; nothing else in
+// this file uses M0.
+__device__ __forceinline__ void dma16(i32x4 rsrc, int voffset, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(i32x4 rsrc, int voffset, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (N < 16) with the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * 64;
@@ -302,21 +337,24 @@ constexpr int kDkdvThreads = kDkdvWaves * 64;
 //     which it leaves in LDS as the bf16 B operands of the consumer's products;
 //   consumer (waves 4-7) holds the dK^T and dV^T accumulators and, for block
 //     s - 1, adds dO^T P and Q^T dS (A: the transposed tiles from LDS); it also
-//     stages the Q and dO tiles (through registers, kAhead blocks ahead).
+//     stages the Q and dO tiles and the rows' lse2 and D, with loads that
+//     write LDS directly, two blocks ahead.
 // Each wave fits half a SIMD's registers, so the two roles' MFMAs, softmax
 // and loads overlap on the SIMD.  Per iteration s: producers work on block s
-// (tile buffer s % 3, probability buffer s % 2), consumers on block s - 1 and
-// store block s + 1 into tile buffer (s + 1) % 3 (last read in iteration
-// s - 1); one barrier per iteration.
+// (tile buffer s % 4, probability buffer s % 2), consumers on block s - 1;
+// the consumers start the loads of block s + 2 into tile buffer (s + 2) % 4
+// (last read in iteration s - 1) and wait for those of block s + 1 before
+// the iteration's one barrier.
 template <int D, bool VARLEN>
 __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams p) {
   using T = BT<D>;
   constexpr int QTILE = T::PITCH * kBlk;     // bytes of one staged 32-row tile
-  constexpr int kTB = 3;                     // tile buffers (Q, dO, lse2, D)
+  constexpr int kTB = 4;                     // tile buffers (Q, dO, lse2, D)
   constexpr int TBUF = 2 * QTILE + 2 * kBlk * 4;
   constexpr int PW = 2 * 2 * 64 * 16;        // one wave's P and dS operands: [kc][P, dS][lane] x 16 bytes
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kTB * TBUF + 2 * 4 * PW];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kTB * TBUF + 2 * 4 * PW];
   lds_u8* const lds = (lds_u8*)smem;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   constexpr uint32_t pbuf0 = kTB * TBUF;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -446,76 +484,75 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
     return;
   }
 
-  // consumer: stages the tiles (thread ct of 256) and accumulates dK^T, dV^T
-  const int ct = tid - 4 * 64;
+  // consumer: stages the tiles and accumulates dK^T, dV^T
+  const int cw = kw;  // consumer wave 0..3
   f32x16 dkt[T::NDB], dvt[T::NDB];
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) dkt[db] = dvt[db] = f32x16{};
-  // step t's tiles travel in register set t % kAhead, loaded kAhead steps
-  // before they are stored, and sit in tile buffer t % 3
-  struct Set {
-    Stage<D, kBlk> q, o;
-    float l2, d;  // lse2 and D of row ct (ct < 32)
-  };
-  Set sets[kAhead];
-  const StageOff<D, kBlk> so(q_row, ct);
-  // Every call issues the same loads, whatever the step (a step past the
-  // last reads zero-size ranges, which touch no memory): with a fixed count
-  // of loads per step the compiler waits, before storing a set, only for
-  // that set's loads, not for the two sets fetched after it.  The row
-  // statistics are loaded by every lane (lanes past the block's rows load
-  // its first row again) through ranges that end with row Nq - 1.
-  auto fetch = [&](Set& st, int s) __attribute__((always_inline)) {
-    const bool on = s < steps;
-    const int sc = on ? s : 0;
-    const int h = hk * p.group + sc / nblk;
-    const int i0 = q_first + (sc % nblk) * kBlk;
-    const uint16_t* qb = p.q + sq.q0 * q_row + (int64_t)h * D;
-    const uint16_t* ob = p.dout + sq.q0 * q_row + (int64_t)h * D;
-    st.q.load(qb, q_row, i0, Nq, so, on);
-    st.o.load(ob, q_row, i0, Nq, so, on);
-    const int64_t o0 = sq.stat(p, h, VARLEN) + i0;
-    const int sb = on ? min(kBlk, Nq - i0) * 4 : 0;
-    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(p.lse2 + o0, (short)0, sb, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(p.dsum + o0, (short)0, sb, 0x00020000);
-    const int r = (ct < kBlk ? ct : 0) * 4;
-    st.l2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, r, 0, 0));
-    st.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, r, 0, 0));
-  };
-  // the set of step s into tile buffer b; rows past Nq get lse2 = +inf, D = 0
-  auto stash = [&](const Set& st, int b, int s) __attribute__((always_inline)) {
-    st.q.store(lds, b * TBUF, ct);
-    st.o.store(lds, b * TBUF + QTILE, ct);
-    if (ct < kBlk) {
-      const bool row = q_first + (s % nblk) * kBlk + ct < Nq;
-      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + b * TBUF + 2 * QTILE + ct * 4) =
-          row ? st.l2 : __builtin_inff();
-      *reinterpret_cast<__attribute__((address_space(3))) float*>(lds + b * TBUF + 2 * QTILE + kBlk * 4 + ct * 4) =
-          row ? st.d : 0.f;
+  // Block t lands in tile buffer t % 4.  Each 1 KiB load of a tile fills LDS
+  // bytes [1024 i, 1024 i + 1024) of it: lane L's 16 bytes go to row
+  // r = (1024 i + 16 L) / PITCH, physical piece c, so the lane fetches logical
+  // piece c ^ swz(r) of row r (the swizzled layout the fragment reads
+  // expect).  Consumer wave cw issues loads cw * LPT .. + LPT - 1 of each
+  // tile; waves 0 and 1 also load the block's lse2 and D (half a wave each).
+  // Rows past Nq read as zero: zero Q and dO rows add nothing to dK and dV
+  // whatever their probabilities, and lse2 = D = 0 keeps those finite.
+  constexpr int NLD = QTILE / 1024;  // loads per tile
+  constexpr int LPT = NLD / 4;       // per consumer wave
+  static_assert(LPT * 4 == NLD, "every consumer wave moves the same share of a tile");
+  int voff[LPT];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int pos = (cw * LPT + j) * 1024 + lane * 16;
+    const int r = pos / T::PITCH, c = (pos % T::PITCH) >> 4;
+    voff[j] = r * (int)(q_row * 2) + ((c ^ T::swz(r)) << 4);
+  }
+  // the loads of block t into tile buffer `buf`; past the last block they
+  // read zero-size ranges, so every wave issues the same loads every step
+  auto issue = [&](int t, int buf) __attribute__((always_inline)) {
+    const bool on = t < steps;
+    const int tc = on ? t : 0;
+    const int h = hk * p.group + tc / nblk;
+    const int i0 = q_first + (tc % nblk) * kBlk;
+    const int real = min(kBlk, Nq - i0);  // rows of the block that exist (>= 1 if on)
+    const uint32_t bytes = on ? (uint32_t)((real - 1) * q_row * 2 + 2 * D) : 0u;
+    const int64_t row0 = (sq.q0 + i0) * q_row + (int64_t)h * D;
+    const i32x4 rq = dma_rsrc(p.q + row0, bytes), ro = dma_rsrc(p.dout + row0, bytes);
+    const uint32_t lb = lds0 + (uint32_t)buf * TBUF + (uint32_t)cw * LPT * 1024;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) dma16(rq, voff[j], lb + j * 1024);
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) dma16(ro, voff[j], lb + QTILE + j * 1024);
+    if (cw < 2) {
+      const float* st = (cw == 0 ? p.lse2 : p.dsum) + sq.stat(p, h, VARLEN) + i0;
+      const i32x4 rs = dma_rsrc(st, on ? (uint32_t)real * 4 : 0u);
+      const uint32_t ls = lds0 + (uint32_t)buf * TBUF + 2 * QTILE + (uint32_t)cw * kBlk * 4;
+      if (lane < kBlk) dma4(rs, lane * 4, ls);
     }
   };
-  static_assert(kAhead == kTB, "one register set and one tile buffer per step modulo 3");
-  unroll_while<0, kAhead>([&](auto J) { fetch(sets[J], J); return true; });
-  if (steps > 0) stash(sets[0], 0, 0);
-  fetch(sets[0], kAhead);
+  // this wave's loads of the older of the two blocks in flight have landed
+  auto wait_older = [&]() __attribute__((always_inline)) {
+    if (cw < 2)
+      wait_vm<2 * LPT + 1>();
+    else
+      wait_vm<2 * LPT>();
+  };
+  issue(0, 0);
+  issue(1, 1);
+  wait_older();
   __syncthreads();
-  for (int s0 = 0; s0 <= steps; s0 += kAhead) {
-   const bool more = unroll_while<0, kAhead>([&](auto U) __attribute__((always_inline)) {
-    constexpr int u = decltype(U)::value;  // s % 3
+  for (int s0 = 0; s0 <= steps; s0 += kTB) {
+   const bool more = unroll_while<0, kTB>([&](auto U) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;  // s % 4
     const int s = s0 + u;
     if (s > steps) return false;
-    // block s + 1 into tile buffer (s + 1) % 3, last read in iteration s - 1;
-    // done first, so that the products below run on the matrix cores while
-    // the producer computes its softmax
-    if (s + 1 < steps) stash(sets[(u + 1) % kAhead], (u + 1) % kTB, s + 1);
-    fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
+    issue(s + 2, (u + 2) % kTB);
     if (s >= 1) {
       // dV^T += dO^T P and dK^T += Q^T dS of block s - 1
       bool any, full;
       block_case(s - 1, any, full);
       if (any) {
-        constexpr int bp = (u + kTB - 1) % kTB;  // tile buffer of block s - 1
-        const uint32_t qoff = bp * TBUF, ooff = qoff + QTILE;
+        constexpr uint32_t qoff = (uint32_t)((u + kTB - 1) % kTB) * TBUF, ooff = qoff + QTILE;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
           const bf16x8 bpv = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + pb(s - 1, kc, 0));
@@ -528,6 +565,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
         }
       }
     }
+    wait_older();  // block s + 1, read by the producers after this barrier
     __syncthreads();
     return true;
    });
