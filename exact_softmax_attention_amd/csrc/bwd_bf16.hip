@@ -85,10 +85,8 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-constexpr int kBwdWaves = 4;
-constexpr int kBwdThreads = kBwdWaves * 64;
+constexpr int kTileBlocks = 4;  // 32-row blocks per 128-row tile, one per producer wave
 constexpr int kBlk = 32;  // MFMA block: 32 keys x 32 query rows
-constexpr int kAhead = 3; // tiles whose global loads are in flight (in registers)
 
 // f(integral_constant<0>) .. f(integral_constant<N-1>) while f returns true;
 // the index is a compile-time constant, so register sets can be chosen by it.
@@ -162,7 +160,7 @@ __device__ __forceinline__ SeqTile seq_tile(const BwdParams& p, const Wg& w, con
                                             int total, int lane) {
   SeqTile t;
   if constexpr (VARLEN) {
-    constexpr int TILE = kBwdWaves * kBlk;
+    constexpr int TILE = kTileBlocks * kBlk;
     const int slot = w.x;
     t.b = find_seq<TILE>(cu, p.n_seqs, total, slot, lane);
     const int q0 = clampi(p.cu_q[t.b], 0, p.total_q);
@@ -210,52 +208,6 @@ struct BT {
 
 // ---------------------------------------------------------------------------
 // Shared tile helpers.
-
-// Stage ROWS rows (16-byte pieces) of a [N, H, D] tensor starting at row r0
-// into registers: piece p of the block = row p / PIECES, piece p % PIECES.
-// The loads are buffer loads whose range ends with row n_rows - 1, so rows at
-// or past n_rows read as zero; each thread's byte offsets within the block
-// are fixed (StageOff) and only the scalar base moves from step to step.
-template <int D, int ROWS>
-struct StageOff {
-  static constexpr int NP = ROWS * BT<D>::PIECES / kBwdThreads;  // pieces per thread
-  static_assert(NP * kBwdThreads == ROWS * BT<D>::PIECES, "whole pieces per thread");
-  int off[NP];
-  __device__ __forceinline__ StageOff(int64_t row_stride, int tid) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int p = tid + i * kBwdThreads;
-      off[i] = (int)((p / BT<D>::PIECES) * row_stride * 2) + (p % BT<D>::PIECES) * 16;
-    }
-  }
-};
-
-template <int D, int ROWS>
-struct Stage {
-  static constexpr int NP = StageOff<D, ROWS>::NP;
-  u32x4 r[NP];
-  // on = false: a zero-size range, which reads nothing and gives zeros (the
-  // callers issue the same loads every step, see the consumers' fetch)
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t row_stride, int r0, int n_rows,
-                                       const StageOff<D, ROWS>& so, bool on) {
-    const int real = min(ROWS, n_rows - r0);  // rows of the block that exist (>= 1 if on)
-    const int bytes = on ? (int)((real - 1) * row_stride * 2) + 2 * D : 0;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(base + (int64_t)r0 * row_stride), (short)0, bytes, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < NP; ++i)
-      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, so.off[i], 0, 0));
-  }
-  __device__ __forceinline__ void store(lds_u8* lds, uint32_t off, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int p = tid + i * kBwdThreads;
-      const int row = p / BT<D>::PIECES, pc = p % BT<D>::PIECES;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-          lds + off + row * BT<D>::PITCH + ((pc ^ BT<D>::swz(row)) << 4)) = r[i];
-    }
-  }
-};
 
 // A operand (rows x k) of a 32x32x16 MFMA from a staged tile: lane l reads row
 // l % 32, features 16c + 8 (l / 32) .. +7 (piece 2c + l / 32 of the row).
@@ -609,10 +561,12 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
   using T = BT<D>;
   constexpr int KN = 64;                  // keys per step (two 32-key blocks)
   constexpr int KTILE = T::PITCH * KN;    // bytes of one staged K or V tile
-  constexpr int kTB = 3;                  // tile buffers
+  constexpr int kTB = 4;                  // tile buffers (K and V)
   constexpr int PW = 2 * 2 * 64 * 16;     // one wave's dS^T operands: [block][kc][lane] x 16 bytes
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kTB * 2 * KTILE + 2 * 4 * PW];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kTB * 2 * KTILE + 2 * 4 * PW];
+  static_assert(sizeof(smem) <= 160 * 1024, "LDS budget");
   lds_u8* const lds = (lds_u8*)smem;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   constexpr uint32_t pbuf0 = kTB * 2 * KTILE;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -736,49 +690,57 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
     return;
   }
 
-  // consumer: stages the K/V tiles (thread ct of 256) and accumulates dQ^T
-  const int ct = tid - 4 * 64;
+  // consumer: stages the K/V tiles and accumulates dQ^T
+  const int cw = rw;  // consumer wave 0..3
   f32x16 dqt[T::NDB];
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) dqt[db] = f32x16{};
-  // step t's K and V tiles travel in register set t % kAhead and sit in tile buffer t % 3
-  struct Set {
-    Stage<D, KN> k, v;
-  };
-  Set sets[kAhead];
+  // Step t's K and V tiles land in tile buffer t % 4 through loads that write
+  // LDS directly, each lane fetching the swizzled piece that belongs at its
+  // LDS position (as in the dK/dV kernel); consumer wave cw issues loads
+  // cw * LPT .. + LPT - 1 of each tile.  Keys past Nk read as zero, and zero
+  // K and V rows add nothing to dQ.
+  constexpr int NLD = KTILE / 1024;  // loads per tile
+  constexpr int LPT = NLD / 4;       // per consumer wave
+  static_assert(LPT * 4 == NLD, "every consumer wave moves the same share of a tile");
+  int voff[LPT];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int pos = (cw * LPT + j) * 1024 + lane * 16;
+    const int r = pos / T::PITCH, c = (pos % T::PITCH) >> 4;
+    voff[j] = r * (int)(kv_row * 2) + ((c ^ T::swz(r)) << 4);
+  }
   const uint16_t* kbase = p.k + sq.k0 * kv_row + (int64_t)hk * D;
   const uint16_t* vbase = p.v + sq.k0 * kv_row + (int64_t)hk * D;
-  const StageOff<D, KN> so(kv_row, ct);
-  // the same loads every step, as in the dK/dV kernel (a step past the last
-  // reads zero-size ranges)
-  auto fetch = [&](Set& st, int s) __attribute__((always_inline)) {
-    const bool on = s < steps;
-    const int j0 = j_first + (on ? s : 0) * KN;
-    st.k.load(kbase, kv_row, j0, Nk, so, on);
-    st.v.load(vbase, kv_row, j0, Nk, so, on);
+  // the loads of step t into tile buffer `buf`; past the last step they read
+  // zero-size ranges, so every wave issues the same loads every step
+  auto issue = [&](int t, int buf) __attribute__((always_inline)) {
+    const bool on = t < steps;
+    const int j0 = j_first + (on ? t : 0) * KN;
+    const int real = min(KN, Nk - j0);  // keys of the step that exist (>= 1 if on)
+    const uint32_t bytes = on ? (uint32_t)((real - 1) * kv_row * 2 + 2 * D) : 0u;
+    const i32x4 rk = dma_rsrc(kbase + (int64_t)j0 * kv_row, bytes);
+    const i32x4 rv = dma_rsrc(vbase + (int64_t)j0 * kv_row, bytes);
+    const uint32_t lb = lds0 + (uint32_t)buf * 2 * KTILE + (uint32_t)cw * LPT * 1024;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) dma16(rk, voff[j], lb + j * 1024);
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) dma16(rv, voff[j], lb + KTILE + j * 1024);
   };
-  auto stash = [&](const Set& st, int b) __attribute__((always_inline)) {
-    st.k.store(lds, (2 * b) * KTILE, ct);
-    st.v.store(lds, (2 * b + 1) * KTILE, ct);
-  };
-  static_assert(kAhead == kTB, "one register set and one tile buffer per step modulo 3");
-  unroll_while<0, kAhead>([&](auto J) { fetch(sets[J], J); return true; });
-  if (steps > 0) stash(sets[0], 0);
-  fetch(sets[0], kAhead);
+  issue(0, 0);
+  issue(1, 1);
+  wait_vm<2 * LPT>();  // step 0's tiles (step 1's may be in flight)
   __syncthreads();
-  for (int s0 = 0; s0 <= steps; s0 += kAhead) {
-   const bool more = unroll_while<0, kAhead>([&](auto U) __attribute__((always_inline)) {
-    constexpr int u = decltype(U)::value;  // s % 3
+  for (int s0 = 0; s0 <= steps; s0 += kTB) {
+   const bool more = unroll_while<0, kTB>([&](auto U) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;  // s % 4
     const int s = s0 + u;
     if (s > steps) return false;
-    // step s + 1 into tile buffer (s + 1) % 3, last read in iteration s - 1;
-    // done first, so that the products below run on the matrix cores while
-    // the producer computes its softmax
-    if (s + 1 < steps) stash(sets[(u + 1) % kAhead], (u + 1) % kTB);
-    fetch(sets[(u + 1) % kAhead], s + 1 + kAhead);
+    // step s + 2 into tile buffer (s + 2) % 4, last read in iteration s - 1
+    issue(s + 2, (u + 2) % kTB);
     if (s >= 1) {
       constexpr int bp = (u + kTB - 1) % kTB;  // tile buffer of step s - 1
-      const uint32_t koff = (2 * bp) * KTILE;
+      constexpr uint32_t koff = (2 * bp) * KTILE;
 #pragma unroll
       for (int kb2 = 0; kb2 < KN / kBlk; ++kb2) {
         bool any, full;
@@ -795,6 +757,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
         }
       }
     }
+    wait_vm<2 * LPT>();  // step s + 1's tiles, read by the producers after this barrier
     __syncthreads();
     return true;
    });
@@ -895,7 +858,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   p.B = a.B;
   p.Nq = a.Nq;
   p.Nk = a.Nk;
-  constexpr int TILE = kBwdWaves * kBlk;
+  constexpr int TILE = kTileBlocks * kBlk;
   const dim3 g1((a.Nk + TILE - 1) / TILE, a.Hkv, a.B);
   const dim3 g2((a.Nq + TILE - 1) / TILE, a.Hq, a.B);
   return launch_bwd<false>(p, a.d, (long long)a.B * a.Nq * a.Hq, g1, g2, stream);
@@ -911,7 +874,7 @@ hipError_t launch_bwd_bf16_varlen(const BwdVarlenArgs& a, hipStream_t stream) {
   p.total_q = a.total_q;
   p.total_k = a.total_k;
   p.B = 1;
-  constexpr int TILE = kBwdWaves * kBlk;
+  constexpr int TILE = kTileBlocks * kBlk;
   const dim3 g1(a.n_seqs > 0 ? a.total_k / TILE + a.n_seqs : 0, a.Hkv, 1);
   const dim3 g2(a.n_seqs > 0 ? a.total_q / TILE + a.n_seqs : 0, a.Hq, 1);
   return launch_bwd<true>(p, a.d, (long long)a.total_q * a.Hq, g1, g2, stream);
