@@ -237,6 +237,26 @@ __device__ __forceinline__ bf16x8 tr_frag(const lds_u8* lds, uint32_t off, int l
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// A 32 x 32 bf16 tile [row][key] with 64-byte rows, the 8-byte chunk j (keys
+// 4j .. 4j + 3) of row r stored at chunk j ^ (r / 4 % 8): the XOR spreads both
+// the producers' writes (row per lane, 4 keys per write) and the
+// transposing reads below over all 64 banks.
+__device__ __forceinline__ uint32_t ptile_chunk(int row, int chunk) {
+  return (uint32_t)(row * 64 + ((chunk ^ ((row >> 2) & 7)) << 3));
+}
+
+// B operand (rows x keys) of a 32x32x16 MFMA from such a tile, row chunk kc:
+// the transposing read of tr_frag, so lane l gets key l % 32 and rows
+// {4g..4g+3, 8+4g..8+4g+3} + 16 kc, the row order of tr_frag's A operand.
+__device__ __forceinline__ bf16x8 ptile_frag(const lds_u8* lds, uint32_t off, int lane, int kc) {
+  const int G16 = lane >> 4, s16 = lane & 15;
+  const int row = kc * 16 + (G16 >> 1) * 4 + (s16 >> 2);
+  const int chunk = 4 * (G16 & 1) + (s16 & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + off + ptile_chunk(row, chunk)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + off + ptile_chunk(row + 8, chunk)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // ---------------------------------------------------------------------------
 // D and LSE * log2(e) per row.
 
@@ -284,9 +304,11 @@ constexpr int kDkdvThreads = kDkdvWaves * 64;
 // One work group per (128-key tile, KV head, batch), 8 waves in two roles
 // sharing the tile's keys (wave w and w + 4 own keys 32 (w % 4) .. +31 and
 // run on one SIMD):
-//   producer (waves 0-3) holds its keys' K and V rows as B operands and, for
-//     query block s, forms S = Q K^T and dP = dO V^T, then P and dS = P (dP - D),
-//     which it leaves in LDS as the bf16 B operands of the consumer's products;
+//   producer (waves 0-3) holds its keys' K and V rows as A operands and, for
+//     query block s, forms S^T = K Q^T and dP^T = V dO^T (a lane per query
+//     row, so each lane needs one row's lse2 and D), then P and dS = P (dP - D),
+//     which it leaves in LDS as [row][key] bf16 tiles that the consumer reads
+//     with transposing loads as the B operands of its products;
 //   consumer (waves 4-7) holds the dK^T and dV^T accumulators and, for block
 //     s - 1, adds dO^T P and Q^T dS (A: the transposed tiles from LDS); it also
 //     stages the Q and dO tiles and the rows' lse2 and D, with loads that
@@ -303,7 +325,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
   constexpr int QTILE = T::PITCH * kBlk;     // bytes of one staged 32-row tile
   constexpr int kTB = 4;                     // tile buffers (Q, dO, lse2, D)
   constexpr int TBUF = 2 * QTILE + 2 * kBlk * 4;
-  constexpr int PW = 2 * 2 * 64 * 16;        // one wave's P and dS operands: [kc][P, dS][lane] x 16 bytes
+  constexpr int PW = 2 * 32 * 64;            // one wave's P and dS tiles: 32 rows x 64 bytes each
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kTB * TBUF + 2 * 4 * PW];
   lds_u8* const lds = (lds_u8*)smem;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
@@ -344,12 +366,13 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
     full = (!p.causal || kw0 + kBlk - 1 <= i0 + delta) &&
            (p.window <= 0 || i0 + kBlk - 1 + delta - kw0 < p.window);
   };
-  auto pb = [&](int s, int kc, int which) __attribute__((always_inline)) {
-    return pbuf0 + (uint32_t)(s & 1) * 4 * PW + kw * PW + (uint32_t)((kc * 2 + which) * 64 + lane) * 16;
+  // this wave's P (which = 0) or dS (1) tile of block s
+  auto pt = [&](int s, int which) __attribute__((always_inline)) {
+    return pbuf0 + (uint32_t)(s & 1) * 4 * PW + kw * PW + (uint32_t)which * (PW / 2);
   };
 
   if (producer) {
-    // K and V of the lane's key as B operands (features 16c + 8g .. +7)
+    // K and V of the lane's key as A operands (features 16c + 8g .. +7)
     bf16x8 kb[T::KC], vb[T::KC];
     {
       const int64_t off = (sq.k0 + key) * kv_row + (int64_t)hk * D + 8 * g;
@@ -374,60 +397,59 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
           const int b = s % kTB;
           const uint32_t qoff = b * TBUF, ooff = qoff + QTILE;
           const uint32_t loff = qoff + 2 * QTILE, doff = loff + kBlk * 4;
-          // S = Q K^T and dP = dO V^T (lane: key, 16 rows).  All of the
-          // block's operand reads go out before the first product, so that
-          // the products wait for the LDS once rather than once each.
+          // S^T = K Q^T and dP^T = V dO^T: lane l holds query row i0 + n
+          // (n = l % 32) and keys kw0 + 4g + c(r), c(r) = r % 4 + 8 (r / 4).  All
+          // of the block's operand reads go out before the first product, so
+          // that the products wait for the LDS once rather than once each.
+          const int n = lane & 31;
           bf16x8 qa[T::KC], oa[T::KC];
 #pragma unroll
           for (int c = 0; c < T::KC; ++c) {
             qa[c] = row_frag<D>(lds, qoff, lane, c);
             oa[c] = row_frag<D>(lds, ooff, lane, c);
           }
+          const float l2 = *reinterpret_cast<const __attribute__((address_space(3))) float*>(lds + loff + n * 4);
+          const float dd = *reinterpret_cast<const __attribute__((address_space(3))) float*>(lds + doff + n * 4);
           f32x16 sacc = f32x16{}, dpacc = f32x16{};
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int c = 0; c < T::KC; ++c) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c], kb[c], sacc, 0, 0, 0);
-            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[c], vb[c], dpacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[c], qa[c], sacc, 0, 0, 0);
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[c], oa[c], dpacc, 0, 0, 0);
           }
           __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::KC, 0);  // the reads
           __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::KC, 0);  // then the products
+          __builtin_amdgcn_s_setprio(0);
           float pr[16], ds[16];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            // rows 4g + 8t .. +3 of the block: their lse2 and D
-            const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + loff + (4 * g + 8 * t) * 4);
-            const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + doff + (4 * g + 8 * t) * 4);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) pr[4 * t + u] = fast_exp2(sacc[4 * t + u] * p.sl2 - l4[u]);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) ds[4 * t + u] = dpacc[4 * t + u] - d4[u];
-          }
+          for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(sacc[r] * p.sl2 - l2);
           if (!full) {
-            // register r holds row i0 + 4g + c(r), c(r) = r % 4 + 8 (r / 4); with
-            // t = key - (i0 + 4g + delta): hidden by causality when t > c(r), by the
-            // window when t <= c(r) - window
-            const int tk = key - (i0 + 4 * g + delta);
+            // with t = kw0 + 4g - (i0 + n + delta), key kw0 + 4g + c(r) is past
+            // the row's position when t + c(r) > 0 and before its window when
+            // t + c(r) <= -window
+            const int tk = kw0 + 4 * g - (i0 + n + delta);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int c = (r & 3) + 8 * (r >> 2);
-              bool hide = p.causal && tk > c;
-              if (p.window > 0 && tk <= c - p.window) hide = true;
+              bool hide = p.causal && tk + c > 0;
+              if (p.window > 0 && tk + c <= -p.window) hide = true;
               if (hide) pr[r] = 0.f;
             }
           }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) ds[r] *= pr[r];
-          // P and dS as the consumer's B operands, one 16-byte piece per lane
+          for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dpacc[r] - dd);
+          // P and dS into this wave's [row][key] tiles: registers 4t .. 4t + 3
+          // are keys 8t + 4g .. +3, chunk 2t + g of row n
 #pragma unroll
-          for (int kc = 0; kc < 2; ++kc) {
-            u32x4 pp, pd;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              pp[i] = pack_bf16x2(pr[8 * kc + 2 * i], pr[8 * kc + 2 * i + 1]);
-              pd[i] = pack_bf16x2(ds[8 * kc + 2 * i], ds[8 * kc + 2 * i + 1]);
-            }
-            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + pb(s, kc, 0)) = pp;
-            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + pb(s, kc, 1)) = pd;
+          for (int t = 0; t < 4; ++t) {
+            u32x2 pp, pd;
+            pp[0] = pack_bf16x2(pr[4 * t], pr[4 * t + 1]);
+            pp[1] = pack_bf16x2(pr[4 * t + 2], pr[4 * t + 3]);
+            pd[0] = pack_bf16x2(ds[4 * t], ds[4 * t + 1]);
+            pd[1] = pack_bf16x2(ds[4 * t + 2], ds[4 * t + 3]);
+            const uint32_t a = ptile_chunk(n, 2 * t + g);
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds + pt(s, 0) + a) = pp;
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds + pt(s, 1) + a) = pd;
           }
         }
       }
@@ -507,8 +529,8 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
         constexpr uint32_t qoff = (uint32_t)((u + kTB - 1) % kTB) * TBUF, ooff = qoff + QTILE;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          const bf16x8 bpv = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + pb(s - 1, kc, 0));
-          const bf16x8 bdv = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + pb(s - 1, kc, 1));
+          const bf16x8 bpv = ptile_frag(lds, pt(s - 1, 0), lane, kc);
+          const bf16x8 bdv = ptile_frag(lds, pt(s - 1, 1), lane, kc);
 #pragma unroll
           for (int db = 0; db < T::NDB; ++db) {
             dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, ooff, lane, db, kc), bpv, dvt[db], 0, 0, 0);
@@ -650,6 +672,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
             va[c] = row_frag<D>(lds, vb_off, lane, c);
           }
           f32x16 sacc = f32x16{}, dpacc = f32x16{};
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int c = 0; c < T::KC; ++c) {
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qb[c], sacc, 0, 0, 0);
@@ -657,6 +680,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(const BwdParams p)
           }
           __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::KC, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::KC, 0);
+          __builtin_amdgcn_s_setprio(0);
           float pr[16], ds[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(sacc[r] * p.sl2 - l2);
