@@ -35,6 +35,9 @@ SMALL = [
     (1, 512, 512, 2, 1, 128, True, 0),
     (1, 5, 0, 2, 1, 64, False, 0),
     (1, 0, 7, 2, 1, 64, False, 0),
+    # d = 64 through many steps of the staging ring (MQA: 4 heads per key tile)
+    (1, 700, 700, 4, 1, 64, True, 0),
+    (1, 150, 333, 2, 2, 64, False, 0),
 ]
 
 
