@@ -15,29 +15,27 @@
 //   bwd_prep   D = rowsum(dO * O) and LSE * log2(e) per (b, h, row), into the
 //              workspace (a row with LSE = -inf, which sees no key, gets
 //              +inf, so that all its probabilities come out 0).
-//   bwd_dkdv   one work group per (128-key tile, KV head, batch); wave w owns
-//              32 keys, holding them as the B operand of
-//              v_mfma_f32_32x32x16_bf16 (lane l: key l % 32).  It walks the G
-//              query heads and their 32-row query blocks that see the tile:
-//                S  = Q K^T     A = Q rows from LDS, B = K (registers)
-//                dP = dO V^T    A = dO rows from LDS, B = V (registers)
-//              (lane l: key l % 32, 16 query rows), then P, dS, and
+//   bwd_dkdv   one work group per (128-key tile, KV head, batch), eight waves
+//              in two roles on v_mfma_f32_32x32x16_bf16.  Producers (waves
+//              0-3, 32 keys each, K and V held as A operands) form, per 32-row
+//              query block of each of the G query heads,
+//                S^T = K Q^T,  dP^T = V dO^T   B = Q, dO rows from LDS
+//              (lane l: query row l % 32, 16 keys), then P and dS, which go
+//              to LDS as bf16 [row][key] tiles.  Consumers (waves 4-7, on the
+//              same SIMDs) add
 //                dV^T += dO^T P   A = dO^T from the LDS transposing load
-//                dK^T += Q^T dS   A = Q^T likewise
-//              with P and dS converted to bf16 (round to nearest even) as the
-//              B operands straight from the score registers: the MFMA k index
-//              runs over the query rows in the same permuted order on both
-//              operands.
-//   bwd_dq     one work group per 128-row query tile of one head; wave w owns
-//              32 rows, holding Q and dO as B operands (lane l: row l % 32):
-//                S^T = K Q^T,  dP^T = V dO^T   A = K, V rows from LDS
-//                dQ^T += K^T dS^T              A = K^T from the transposing load
-//              so P, D and the log-sum-exp are one value per lane.
-// Tiles go through registers into LDS (double-buffered: the next tile's
-// global loads are in flight while the current one is computed).  The
-// 16-byte pieces of a staged row are XOR-swizzled (BT::swz), which keeps both
-// the row reads and the transposing reads of the same tile free of bank
-// conflicts.
+//                dK^T += Q^T dS   A = Q^T likewise, B = the tiles, read with
+//              the same transposing load so that the MFMA k index runs over
+//              the query rows in the same permuted order on both operands.
+//   bwd_dq     one work group per 128-row query tile of one head, the same
+//              two roles: producers hold Q and dO as B operands (lane l: row
+//              l % 32) and form S^T = K Q^T, dP^T = V dO^T and dS^T over
+//              64-key steps (A = K, V rows from LDS); consumers add
+//              dQ^T += K^T dS^T (A = K^T from the transposing load).
+// The consumers stage the tiles with buffer loads that write LDS directly,
+// two steps ahead of their use.  The 16-byte pieces of a staged row are
+// XOR-swizzled (BT::swz), which keeps both the row reads and the transposing
+// reads of the same tile free of bank conflicts.
 #include <type_traits>
 
 #include "device_common.h"
