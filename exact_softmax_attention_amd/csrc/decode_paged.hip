@@ -29,7 +29,8 @@
 //                 probabilities (bf16, round to nearest even), A = V^T read
 //                 with the transposing LDS load from the block's V rows, which
 //                 the wave stages in its own LDS slot.
-// The next block's K/V loads are in flight while a block is computed.
+// The next block's K/V loads are in flight while a block is computed; they are
+// non-temporal loads (the cache is streamed once per call).
 //
 // Kernel 2 (combine): one work group per (sequence, query head); 4 waves each
 // take every 4th partial, rescale to the common maximum and sum in a fixed
@@ -186,11 +187,15 @@ __global__ __launch_bounds__(64 * kGroupWaves) void decode_split_kernel(const Pa
       const int64_t base = (int64_t)phys * kBlock * row_elems;
       const uint16_t* kp = p.kc + base + koff;
       const uint16_t* vp = p.vc + base + voff;
+      // non-temporal: the cache is read once per call, so its lines should not
+      // displace (or force the write-back of) what the caches hold
 #pragma unroll
-      for (int c = 0; c < T::KC; ++c) rk[c] = *reinterpret_cast<const u32x4*>(kp + 32 * c);
+      for (int c = 0; c < T::KC; ++c)
+        rk[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * c));
 #pragma unroll
       for (int j = 0; j < T::VI; ++j)
-        rv[j] = *reinterpret_cast<const u32x4*>(vp + (int64_t)j * T::RPI * row_elems);
+        rv[j] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(vp + (int64_t)j * T::RPI * row_elems));
     };
     int id_b = trow[min(1, count - 1)], id_c = trow[min(2, count - 1)];
     fetch(trow[0], kA, vA);

@@ -51,8 +51,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     const long long b = bi / p.N;
     const long long li = (b * p.H + h) * p.N + i;  // [B, H, N]
     const float la = p.la[li], lb = p.lb[li];
-    const u32x4 xa = *reinterpret_cast<const u32x4*>(p.oa + r * D + sub * 8);
-    const u32x4 xb = *reinterpret_cast<const u32x4*>(p.ob + r * D + sub * 8);
+    // O is read once (non-temporal); the LSE lines serve the neighbouring rows
+    const u32x4 xa = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.oa + r * D + sub * 8));
+    const u32x4 xb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.ob + r * D + sub * 8));
     const bool nan = la != la || lb != lb;
     const float m = fmaxf(la, lb);
     float wa = 0.f, wb = 0.f;

@@ -13,7 +13,9 @@
 //                2 KiB stride), the 8 waves of a work group streaming their
 //                slices of the same blocks without synchronising
 // Each lane loads 16 bytes at a time with DEPTH blocks in flight per wave; the
-// data is folded into one word per lane so that no load is dead.
+// data is folded into one word per lane so that no load is dead.  Every
+// pattern is measured with ordinary loads and with non-temporal loads (which
+// the decode kernel uses: the cache is streamed once per call).
 //
 // Build: hipcc --offload-arch=gfx950 -O3 -o read_ceiling read_ceiling.hip
 // Run:   ./read_ceiling      (one JSON line on stdout)
@@ -34,7 +36,13 @@ constexpr int kReadBlocks = 37184;           // 1.2185 GB
 constexpr int kThreads = 512;                // 8 waves
 
 // whole blocks: a work group reads one block per step (each lane 4 pieces)
-template <int DEPTH>
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int DEPTH, bool NT>
 __global__ __launch_bounds__(kThreads) void read_whole(const u32x4* __restrict__ pool,
                                                        const int* __restrict__ ids, int n,
                                                        unsigned* __restrict__ sink) {
@@ -47,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void read_whole(const u32x4* __restrict__
       const int bb = min(b + d * (int)gridDim.x, n - 1);
       const u32x4* p = pool + (size_t)ids[bb] * kBlockVec + tid;
 #pragma unroll
-      for (int j = 0; j < kBlockVec / kThreads; ++j) r[d][j] = p[j * kThreads];
+      for (int j = 0; j < kBlockVec / kThreads; ++j) r[d][j] = ld<NT>(p + j * kThreads);
     }
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
@@ -59,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void read_whole(const u32x4* __restrict__
 
 // per-head slices: wave h reads bytes [256 h, 256 h + 256) of each of the
 // block's 16 rows of 2 KiB (lane: row lane / 16 + 4 i, piece lane % 16)
-template <int DEPTH>
+template <int DEPTH, bool NT>
 __global__ __launch_bounds__(kThreads) void read_heads(const u32x4* __restrict__ pool,
                                                        const int* __restrict__ ids, int n,
                                                        unsigned* __restrict__ sink) {
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void read_heads(const u32x4* __restrict__
       const int bb = min(b + d * (int)gridDim.x, n - 1);
       const u32x4* p = pool + (size_t)ids[bb] * kBlockVec + off;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[d][i] = p[i * 4 * 128];  // rows 4 i .. 4 i + 3
+      for (int i = 0; i < 4; ++i) r[d][i] = ld<NT>(p + i * 4 * 128);  // rows 4 i .. 4 i + 3
     }
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
@@ -135,12 +143,17 @@ int main() {
     }
     return best;
   };
-  const double contiguous = std::max(best_of(read_whole<2>, seq), best_of(read_whole<4>, seq));
-  const double random = std::max(best_of(read_whole<2>, perm), best_of(read_whole<4>, perm));
-  const double heads = std::max(best_of(read_heads<2>, perm), best_of(read_heads<4>, perm));
+  const double contiguous = std::max(best_of(read_whole<2, false>, seq), best_of(read_whole<4, false>, seq));
+  const double random = std::max(best_of(read_whole<2, false>, perm), best_of(read_whole<4, false>, perm));
+  const double heads = std::max(best_of(read_heads<2, false>, perm), best_of(read_heads<4, false>, perm));
+  const double contiguous_nt = std::max(best_of(read_whole<2, true>, seq), best_of(read_whole<4, true>, seq));
+  const double random_nt = std::max(best_of(read_whole<2, true>, perm), best_of(read_whole<4, true>, perm));
+  const double heads_nt = std::max(best_of(read_heads<2, true>, perm), best_of(read_heads<4, true>, perm));
   std::printf("{\"bytes\": %lld, \"contiguous_GBps\": %.1f, \"random_blocks_GBps\": %.1f, "
-              "\"per_head_slices_GBps\": %.1f}\n",
-              (long long)kReadBlocks * kBlockBytes, contiguous, random, heads);
+              "\"per_head_slices_GBps\": %.1f, \"contiguous_nt_GBps\": %.1f, "
+              "\"random_blocks_nt_GBps\": %.1f, \"per_head_slices_nt_GBps\": %.1f}\n",
+              (long long)kReadBlocks * kBlockBytes, contiguous, random, heads, contiguous_nt,
+              random_nt, heads_nt);
   CHECK(hipFree(pool));
   CHECK(hipFree(ids));
   CHECK(hipFree(sink));
