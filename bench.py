@@ -106,7 +106,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # after an idle spell the GPU's clock ramps up over the first 10-15 launches
+    # (about 20-40 ms of work); 25 untimed steps put every timed region past it
+    ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default=None,
                     help="time only this dense workload's forward (extra lines)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
@@ -461,7 +463,7 @@ def main():
             attn_bwd(qd, kd, vd, out, do, lse, causal=cfg.causal, window=cfg.window,
                      scale=cfg.scale, dq=dq, dk=dk, dv=dv, workspace=bws)
 
-        bper, _ = time_loop([bwd], max(2, args.steps // 2), max(1, args.warmup), torch)
+        bper, _ = time_loop([bwd], max(2, args.steps // 2), max(1, args.warmup // 2), torch)
         bflops = metrics.bwd_flops(cfg.B, cfg.Hq, cfg.Nq, cfg.Nk, cfg.d, cfg.causal, cfg.window)
         btf = bflops / (bper[0] * 1e-3) / 1e12
         res["backward"] = {"value": round(btf, 2), "unit": "TFLOP/s", "ms": round(bper[0], 4),
@@ -509,7 +511,7 @@ def main():
                             window=vc.window, scale=vc.scale, dq=pdq, dk=pdk, dv=pdv,
                             workspace=pws)
 
-        vbper, _ = time_loop([varlen_bwd], max(2, args.steps // 2), max(1, args.warmup), torch)
+        vbper, _ = time_loop([varlen_bwd], max(2, args.steps // 2), max(1, args.warmup // 2), torch)
         lens = (cu_q[1:] - cu_q[:-1]).cpu().numpy()
         vflops = metrics.varlen_fwd_flops(lens, lens, vc.Hq, vc.d, vc.causal, vc.window)
         padded = metrics.fwd_flops(len(lens), vc.Hq, vc.max_len, vc.max_len, vc.d, vc.causal,
