@@ -267,8 +267,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
   // rows in [B, Nq, Hq] (packed: [total_q, Hq]) order
   const int64_t rows = VARLEN ? (int64_t)p.total_q * p.Hq : (int64_t)p.B * p.Nq * p.Hq;
   for (int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR; r < rows; r += (int64_t)gridDim.x * RPB) {
+    // O is read once (non-temporal); dO is read again by the dK/dV and dQ kernels
     const u32x4 a = *reinterpret_cast<const u32x4*>(p.dout + r * D + sub * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(p.o + r * D + sub * 8);
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.o + r * D + sub * 8));
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)

@@ -942,9 +942,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
 // Paged chunked prefill, second pass: rows of items done in several key
 // chunks merge the chunks' (O_c, LSE_c): M = max LSE_c, w_c = exp(LSE_c - M),
 // O = sum w_c O_c / sum w_c, LSE = M + ln sum w_c (the exact merge of partial
-// softmax states).  One work group per (schedule slot, query head); a wave
-// per row at a time, the lanes along the features.  A NaN partial (a block
-// the first pass could not read) gives NaN.
+// softmax states), taken in one pass: the running (m, sum, O) of a row is
+// rescaled whenever a chunk raises its maximum, so a row's chunks are read in
+// one round of loads.  One work group per (schedule slot, query head); a wave
+// takes 8 rows at a time, the lanes along the features, with the loads of all
+// their chunks (up to 4 at a time) in flight together; the partials are read
+// once, with non-temporal loads.  A NaN partial (a block the first pass could
+// not read) gives NaN.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(const Params p) {
   const int lane = threadIdx.x & 63;
@@ -965,60 +969,48 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const Params p) {
   const int c1 = (tr.t_begin + tr.n_tiles - 1) / p.chunk_tiles;
   if (c1 == c0) return;  // written directly by the first pass
   constexpr int F = D / 64;  // features per lane
-  constexpr int R = 4;       // rows of a wave in flight together
+  constexpr int R = 8;       // rows of a wave in flight together
   constexpr int CG = 4;      // chunks whose loads are issued together
+  typedef float fF __attribute__((ext_vector_type(F)));
   const int64_t base = (int64_t)(h * p.vtiles + slot) * p.chunks * kBM;
   const int64_t q_row = (int64_t)p.Hq * D;
   const int nrows = min(kBM, Nq - qt * kBM);
   for (int r0 = wave * R; r0 < nrows; r0 += 4 * R) {
-    // pass 1: the largest LSE of each row (NaN noted separately: fmaxf drops it)
-    float m[R];
+    float m[R], sum[R];
+    fF o[R];
     bool nan[R];
   #pragma unroll
     for (int i = 0; i < R; ++i) {
       m[i] = kNegInf;
+      sum[i] = 0.f;
+      o[i] = fF{};
       nan[i] = false;
     }
     for (int cb = c0; cb <= c1; cb += CG) {
       float l[R][CG];
-  #pragma unroll
-      for (int i = 0; i < R; ++i)
-  #pragma unroll
-        for (int j = 0; j < CG; ++j)
-          l[i][j] = (cb + j <= c1 && r0 + i < nrows)
-                        ? p.part_lse[base + (int64_t)(cb + j) * kBM + r0 + i] : kNegInf;
-  #pragma unroll
-      for (int i = 0; i < R; ++i)
-  #pragma unroll
-        for (int j = 0; j < CG; ++j) {
-          nan[i] |= l[i][j] != l[i][j];
-          m[i] = fmaxf(m[i], l[i][j]);
-        }
-    }
-    // pass 2: weights and the weighted sum of the chunks' O
-    float o[R][F] = {};
-    float sum[R] = {};
-    for (int cb = c0; cb <= c1; cb += CG) {
-      float w[R][CG];
-      float v[R][CG][F];
+      fF v[R][CG];
   #pragma unroll
       for (int i = 0; i < R; ++i)
   #pragma unroll
         for (int j = 0; j < CG; ++j) {
           const bool ok = cb + j <= c1 && r0 + i < nrows;
           const int64_t pr = base + (int64_t)(cb + j) * kBM + r0 + i;
-          w[i][j] = ok ? p.part_lse[pr] : kNegInf;
-  #pragma unroll
-          for (int f = 0; f < F; ++f) v[i][j][f] = ok ? p.part_o[pr * D + lane * F + f] : 0.f;
+          l[i][j] = ok ? __builtin_nontemporal_load(p.part_lse + pr) : kNegInf;
+          v[i][j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const fF*>(p.part_o + pr * D + lane * F))
+                       : fF{};
         }
   #pragma unroll
       for (int i = 0; i < R; ++i)
   #pragma unroll
         for (int j = 0; j < CG; ++j) {
-          const float wt = m[i] == kNegInf ? 0.f : fast_exp2((w[i][j] - m[i]) * kLog2e);
-          sum[i] += wt;
-  #pragma unroll
-          for (int f = 0; f < F; ++f) o[i][f] += wt * v[i][j][f];
+          const float lj = l[i][j];
+          nan[i] |= lj != lj;
+          const float mn = fmaxf(m[i], lj);  // fmaxf passes over a NaN
+          const float a = m[i] == kNegInf ? 0.f : fast_exp2((m[i] - mn) * kLog2e);
+          const float w = !(lj > kNegInf) ? 0.f : fast_exp2((lj - mn) * kLog2e);
+          sum[i] = sum[i] * a + w;
+          o[i] = o[i] * a + v[i][j] * w;
+          m[i] = mn;
         }
     }
   #pragma unroll
