@@ -605,9 +605,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     constexpr int NPV = T::VC * T::NDB;  // MFMAs of the P V update
     constexpr int LA = 8;                // MFMAs whose operands are read ahead
     static_assert(LA <= NQK, "the read-ahead starts with score operands");
-    // K fragment i (= kb * KC + kc) of the tile in K slot `slot`
+    // Score MFMA i takes k-chunk kc = i / NKB of key block kb = i % NKB: the
+    // key blocks of one k-chunk are issued back to back, so consecutive MFMAs
+    // share their Q operand (fewer operand bits switch: the kernel is power
+    // limited).  K fragment i of the tile in K slot `slot`:
     auto kfrag = [&](int slot, int i) __attribute__((always_inline)) {
-      const uint32_t a = (kfrag0 ^ ((i % T::KC) << 5)) + slot * T::TILEB + (i / T::KC) * 32 * T::ROWB;
+      const int kc = i / T::NKB, kb = i % T::NKB;
+      const uint32_t a = (kfrag0 ^ (kc << 5)) + slot * T::TILEB + kb * 32 * T::ROWB;
       return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + a);
     };
     // score operands read ahead across the barrier, at the end of the V
@@ -667,8 +671,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
         vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       auto qk_mfma = [&](int i) __attribute__((always_inline)) {  // the first k-chunk starts from zero
-        st[i / T::KC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            kf[i], qf[i % T::KC], i % T::KC == 0 ? f32x16{} : st[i / T::KC], 0, 0, 0);
+        const int kc = i / T::NKB, kb = i % T::NKB;
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[kc], kc == 0 ? f32x16{} : st[kb],
+                                                         0, 0, 0);
       };
       auto pv_mfma = [&](int i) __attribute__((always_inline)) {
         const int kc = i / T::NDB, db = i % T::NDB;
