@@ -530,11 +530,14 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const BwdParams 
         for (int kc = 0; kc < 2; ++kc) {
           const bf16x8 bpv = ptile_frag(lds, pt(s - 1, 0), lane, kc);
           const bf16x8 bdv = ptile_frag(lds, pt(s - 1, 1), lane, kc);
+          // the four dV products, then the four dK products: consecutive
+          // products share their B operand (fewer switching bits)
 #pragma unroll
-          for (int db = 0; db < T::NDB; ++db) {
+          for (int db = 0; db < T::NDB; ++db)
             dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, ooff, lane, db, kc), bpv, dvt[db], 0, 0, 0);
+#pragma unroll
+          for (int db = 0; db < T::NDB; ++db)
             dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(lds, qoff, lane, db, kc), bdv, dkt[db], 0, 0, 0);
-          }
         }
       }
     }
