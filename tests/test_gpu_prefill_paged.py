@@ -75,6 +75,9 @@ SPLIT = [
     ([9000, 300, 20000], [100, 300, 257], 4, 2, 128, 0),
     ([16385, 8193], [600, 1], 2, 1, 64, 0),
     ([20000, 12000], [300, 260], 4, 4, 128, 9000),  # windows across a chunk boundary
+    # window starts 8101..8356 straddle the 8192-key chunk boundary inside one
+    # query tile: part of its rows see nothing of chunk 0 (partial LSE = -inf)
+    ([9356, 600], [256, 100], 4, 2, 128, 1000),
 ]
 
 
