@@ -132,7 +132,8 @@ constexpr int kBlockTokens = 16;  // tokens per cache block
 constexpr int kChunkTiles = 128;  // paged: 64-key tiles per key chunk (8192 keys)
 
 // Key tiles (64 keys) that query rows [i0, i0 + kBM) of a sequence with Nq
-// queries and Nk keys may see: [t_begin, t_begin + n_tiles).
+// queries and Nk keys may see: [t_begin, t_begin + n_tiles).  i0 may be
+// negative (packed sequences' tiles end at the sequence's last row).
 struct TileRange {
   int t_begin, n_tiles;
 };
@@ -141,7 +142,7 @@ __device__ __forceinline__ TileRange tile_range(int i0, int Nq, int Nk, int caus
   int kv_end = Nk;
   if (causal) kv_end = min(Nk, i0 + kBM + delta);
   int kv_begin = 0;
-  if (window > 0) kv_begin = max(0, i0 + delta - window + 1);
+  if (window > 0) kv_begin = max(0, max(i0, 0) + delta - window + 1);  // rows below 0 do not exist
   TileRange r;
   r.t_begin = kv_begin / 64;
   r.n_tiles = kv_end > kv_begin ? (kv_end + 63) / 64 - r.t_begin : 0;
@@ -281,7 +282,9 @@ __device__ __forceinline__ bool unrolled_while(F&& f) {
 // large: when a lane's partial row sum of the tile exceeds 2^8 (or is not
 // finite, as on a row's first visible tile), the tile is redone with the true
 // row maximum, and the accumulator and sum are rescaled.  Most tiles skip
-// the row maximum altogether.
+// the row maximum altogether.  The decision is the row's own (the wave takes
+// the slow path when any row needs it, but only those rows raise), so a row's
+// results do not depend on which rows share its wave or its query tile.
 //
 // POS_SCALE: scale > 0, so the row maximum of scale*s is scale * max(s) and the
 // scaling folds into the exponent's FMA.  Otherwise every score is scaled first.
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     if (PAGED && tid == 0) s_bad = 0;  // read by the previous item before the unit's last barrier
     // this item: query tile qt of head h of sequence b, whose Nq query rows
     // start at token row q_tok0 and Nk key rows at k_tok0
-    int b, h, qt, Nq, Nk;
+    int b, h, qt, Nq, Nk, i0;
     int64_t q_tok0, k_tok0, lse0;
     bool bad = false;  // paged: a length or block id the kernel cannot read
     int slot = 0, chunk = 0;  // packed: schedule slot; paged: key chunk
@@ -402,11 +405,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
         break;
       }
       qt = ntl - 1 - off;
+      // Packed sequences: the tiles end at the sequence's last row (tile off
+      // holds rows [Nq - (off + 1) kBM, Nq - off kBM)), so the partial tile
+      // holds the first rows, which see the fewest keys under a causal mask;
+      // its rows below 0 do not exist (never stored).  The paged mode keeps
+      // tiles from row 0 (its chunk merge addresses rows by tile).
+      i0 = PAGED ? qt * kBM : Nq - (off + 1) * kBM;
       q_tok0 = q0;
       k_tok0 = k0;
       lse0 = (int64_t)h * p.total_q + q0;
     } else {
       qt = p.pairing ? (e == 0 ? nq - 1 - j : j) : nq - 1 - (per_head - 1 - j);
+      i0 = qt * kBM;
       b = bh / p.Hq;
       h = bh - b * p.Hq;
       Nq = p.Nq;
@@ -416,7 +426,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       lse0 = ((int64_t)b * p.Hq + h) * Nq;
     }
     const int hk = h / p.group;
-    const int i0 = qt * kBM;
     const int qw0 = i0 + wave * kRowsPerWave;
     const int delta = Nk - Nq;
 
@@ -445,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     const int64_t q_row = (int64_t)p.Hq * D;
     bf16x8 qf[T::KC];
     {
-      const int row = min(qw0 + n, Nq - 1);  // rows past the end compute garbage, never stored
+      const int row = max(0, min(qw0 + n, Nq - 1));  // rows outside [0, Nq) compute garbage, never stored
       const uint16_t* qp = p.q + (q_tok0 + row) * q_row + (int64_t)h * D + g * 8;
   #pragma unroll
       for (int c = 0; c < T::KC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + c * 16);
@@ -584,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
     }
     auto wave_skips = [&](int k) __attribute__((always_inline)) {
       const int j0 = (t_begin + k) * T::BN;
-      bool skip = qw0 >= Nq;
+      bool skip = qw0 >= Nq || qw0 + kRowsPerWave - 1 < 0;
       if (p.causal && j0 > qw0 + kRowsPerWave - 1 + delta) skip = true;
       if (p.window > 0 && j0 + T::BN - 1 < qw0 + delta - p.window + 1) skip = true;
       return skip;
@@ -775,7 +784,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
         }
         // fast path: against the stored max (m_run = -inf gives inf/NaN sums)
         float ls = exp_tile(m_run);
-        if (__builtin_amdgcn_ballot_w64(!(ls <= kRaise)) != 0) {
+        const bool need = !(ls <= kRaise);
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
           // row max of the scaled scores as a tree
           auto sv = [&](int kb, int r) __attribute__((always_inline)) {
             return POS_SCALE ? st[kb][r] : st[kb][r] * p.sl2;
@@ -798,7 +808,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
             mx = fmaxf(a, bb);
           }
           if (POS_SCALE) mx *= p.sl2;
-          const float m_new = fmaxf(m_run, mx);
+          // only the rows that need it (either half of the row) raise their
+          // maximum; the others keep it (alpha = 1, the same exponentials), so
+          // a row's arithmetic does not depend on the other rows of its wave
+          float na = need ? 1.f : 0.f, nb = na;
+          asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(na), "+v"(nb));
+          const float m_new = fmaxf(na, nb) > 0.f ? fmaxf(m_run, mx) : m_run;
           const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
           l_run *= alpha;
   #pragma unroll
@@ -928,12 +943,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
           const int r = i * RPI + rr;
           const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
               lds + sbase + r * HB + ((cc ^ ((r / RB) & (HP - 1))) * 16));
-          if (qw0 + r < Nq)
+          if (qw0 + r < Nq && qw0 + r >= 0)
             *reinterpret_cast<u32x4*>(p.o + (q_tok0 + qw0 + r) * q_row + (int64_t)h * D + half * (D / 2) + 8 * cc) = w;
         }
       }
       const int row = qw0 + n;
-      if (row < Nq && p.lse != nullptr && g == 0)
+      if (row < Nq && row >= 0 && p.lse != nullptr && g == 0)
         p.lse[lse0 + row] = (PAGED && bad) ? __builtin_nanf("")
                             : l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
     }

@@ -85,6 +85,24 @@ def test_equal_lengths_match_the_dense_kernel_bitwise(causal, window):
     assert torch.equal(lv, ld.cpu().permute(1, 0, 2).reshape(Hq, B * N))
 
 
+@pytest.mark.parametrize("window", [0, 150])
+def test_ragged_lengths_match_per_sequence_dense_calls_bitwise(window):
+    # A row's keys are visited in the same 64-key tiles, in the same order,
+    # whichever 256-row query tile holds it: the packed kernel's tiles end at
+    # each sequence's last row (the partial tile holds its first rows), the
+    # dense kernel's start at row 0, and the results agree bit for bit.
+    lens_q, lens_k = [5, 300, 513, 1000, 257], [5, 300, 700, 1000, 257]
+    Hq, Hkv, d, scale = 4, 2, 128, 0.09
+    q, k, v, cu_q, cu_k = workloads.make_packed(lens_q, lens_k, Hq, Hkv, d, 2250)
+    ov, lv = _run(q, k, v, cu_q, cu_k, True, window, scale)
+    for s_, (nq, nk) in enumerate(zip(lens_q, lens_k)):
+        q0, k0 = int(cu_q[s_]), int(cu_k[s_])
+        od, ld = attn_fwd(q[q0:q0 + nq][None].cuda(), k[k0:k0 + nk][None].cuda(),
+                          v[k0:k0 + nk][None].cuda(), causal=True, window=window, scale=scale)
+        assert torch.equal(ov[q0:q0 + nq], od.cpu()[0]), (s_, nq, nk)
+        assert torch.equal(lv[:, q0:q0 + nq], ld.cpu()[0]), (s_, nq, nk)
+
+
 def test_deterministic():
     lens = workloads.draw_lengths(5000, 600, 2048, 2300)
     q, k, v, cu_q, cu_k = workloads.make_packed(lens, lens, 8, 2, 128, 2300)
