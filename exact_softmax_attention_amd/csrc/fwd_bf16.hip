@@ -287,7 +287,8 @@ __device__ __forceinline__ bool unrolled_while(F&& f) {
 // results do not depend on which rows share its wave or its query tile.
 //
 // POS_SCALE: scale > 0, so the row maximum of scale*s is scale * max(s) and the
-// scaling folds into the exponent's FMA.  Otherwise every score is scaled first.
+// scaling folds into the exponent's FMA.  Otherwise every score is scaled first,
+// before the mask sets hidden scores to -inf.
 template <int D, bool POS_SCALE, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   constexpr bool VARLEN = MODE != kDense;  // queries packed by cu_seqlens
@@ -752,7 +753,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb)
   #pragma unroll
-        for (int r = 0; r < 16; ++r) e[kb][r] = fast_exp2(fmaf(st[kb][r], p.sl2, -mref));
+        for (int r = 0; r < 16; ++r) e[kb][r] = fast_exp2(fmaf(st[kb][r], POS_SCALE ? p.sl2 : 1.f, -mref));
   #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb)
   #pragma unroll
@@ -770,6 +771,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       (void)U;
       if constexpr (PAGED) paged_advance();
       if (vcase != 2) {
+        if constexpr (!POS_SCALE) {
+          // scale <= 0: the scores are scaled before the mask (a masked score
+          // must be -inf after scaling, and -inf times a scale <= 0 is not)
+  #pragma unroll
+          for (int kb = 0; kb < T::NKB; ++kb)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) st[kb][r] *= p.sl2;
+        }
         if (vcase == 1) {
           const int j0 = (t_begin + k) * T::BN;
           const int pos = qw0 + n + delta;  // this lane's row position
@@ -788,7 +797,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
           // row max of the scaled scores as a tree
           auto sv = [&](int kb, int r) __attribute__((always_inline)) {
-            return POS_SCALE ? st[kb][r] : st[kb][r] * p.sl2;
+            return st[kb][r];  // (scale <= 0: already scaled)
           };
           float mq[4];
   #pragma unroll
