@@ -84,6 +84,19 @@ def test_small_shapes(case):
     check_grad(dv, rv, "dv")
 
 
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 50)])
+def test_negative_scale(causal, window):
+    # the forward's variant for scale <= 0 and the gradients' sign of scale
+    B, N, Hq, Hkv, d, scale = 1, 200, 4, 2, 128, -0.09
+    q, k, v = workloads.make_dense(B, Hq, Hkv, N, N, d, 3900)
+    do = workloads.make_dout(B, N, Hq, d, 3900)
+    dq, dk, dv = _run(q, k, v, do, causal, window, scale)
+    rq, rk, rv, _ = oracle.attention_backward(q, k, v, do, scale, causal, window)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
 def test_deterministic():
     """Two calls give the same bits (no atomics)."""
     q, k, v = workloads.make_dense(1, 4, 2, 300, 300, 128, 3100)

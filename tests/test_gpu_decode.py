@@ -104,6 +104,14 @@ def test_gather_selects_the_matching_token_exactly():
         assert torch.equal(out[b, h], want), (b, h, t)
 
 
+def test_negative_scale_decode():
+    inp = workloads.make_paged(3, 8, 2, 128, 16, 120, 40, seed=1990, seq_lens=[300, 17, 600])
+    out, lse = _decode(inp, -0.09, 0)
+    O, L = oracle.decode_paged(inp["q"], inp["kcache"], inp["vcache"], inp["block_table"],
+                               inp["seq_lens"], -0.09, 0)
+    check(out, O, lse, L, "bf16", "decode, scale -0.09")
+
+
 def test_zero_scale_gives_exact_mean_of_small_integers():
     lens = [1, 7, 16, 17, 48]
     inp = workloads.make_paged(5, 4, 2, 64, 16, 40, 4, seed=2300, seq_lens=lens)

@@ -93,6 +93,14 @@ def test_key_chunk_split(case):
     check(out, O, lse, L, "bf16", _ids(case))
 
 
+def test_negative_scale_chunked_prefill():
+    lens, chunks = [700, 9000], [300, 257]   # the second spans two key chunks
+    inp = _make(lens, chunks, 4, 2, 128, 3090)
+    out, lse = _run(inp, -0.09, 0)
+    O, L = _oracle(inp, -0.09, 0)
+    check(out, O, lse, L, "bf16", "chunked prefill, scale -0.09")
+
+
 def test_one_new_token_matches_decode():
     lens = [40, 700, 1234, 16]
     inp = _make(lens, [1] * 4, 8, 2, 128, 3100)

@@ -58,6 +58,15 @@ def test_small_packed(case):
     check(out, O, lse, L, "bf16", _ids(case))
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_non_positive_scale_packed(scale):
+    lens = [5, 300, 513]
+    q, k, v, cu_q, cu_k = workloads.make_packed(lens, lens, 4, 2, 128, 2050)
+    out, lse = _run(q, k, v, cu_q, cu_k, True, 90, scale)
+    O, L = oracle.attention_varlen(q, k, v, cu_q.numpy(), cu_k.numpy(), scale, True, 90)
+    check(out, O, lse, L, "bf16", f"packed scale {scale}")
+
+
 def test_rows_outside_every_sequence_are_not_written():
     # the sequences cover rows 3 .. 3+sum-1 of a longer q; the rest keep a sentinel
     lens = [70, 300]
