@@ -66,18 +66,19 @@ def test_small_shapes(case, dtype):
     check(out, O, lse, L, dtype, _ids(case))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [-0.09, 0.0])
 @pytest.mark.parametrize("causal,window", [(True, 0), (True, 70), (False, 0)])
-def test_non_positive_scale(scale, causal, window):
-    # scale <= 0 takes the kernel variant that scales every score before its
-    # row maximum; scale = 0 weights every visible key equally
+def test_non_positive_scale(scale, causal, window, dtype):
+    # scale <= 0 takes the bf16 kernel's variant that scales every score before
+    # its row maximum; scale = 0 weights every visible key equally
     B, Nq, Nk, Hq, Hkv, d = 2, 300, 333, 4, 2, 128
     seed = 1900
-    print(f"scale {scale} causal {causal} window {window} seed {seed}", flush=True)
-    q, k, v = workloads.make_dense(B, Hq, Hkv, Nq, Nk, d, seed, "bf16")
-    out, lse = _run("bf16", q, k, v, causal, window, scale)
+    print(f"scale {scale} causal {causal} window {window} {dtype} seed {seed}", flush=True)
+    q, k, v = workloads.make_dense(B, Hq, Hkv, Nq, Nk, d, seed, dtype)
+    out, lse = _run(dtype, q, k, v, causal, window, scale)
     O, L = oracle.attention(q, k, v, scale, causal, window)
-    check(out, O, lse, L, "bf16", f"scale {scale} causal {causal} window {window}")
+    check(out, O, lse, L, dtype, f"scale {scale} causal {causal} window {window} {dtype}")
 
 
 def test_f32_single_head_config():
