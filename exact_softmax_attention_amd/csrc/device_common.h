@@ -80,8 +80,10 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x,
 // candidates and the count of passing lanes narrows the range 64-fold.  The
 // result stays in [0, n) whatever cu holds.  A sequence's TILE-row tiles
 // fit in its slots: start(s + 1) - start(s) >= ceil(len(s) / TILE).
-template <int TILE>
-__device__ __forceinline__ int find_seq(const int* cu, int n, int total, int v, int lane) {
+// cu may point to global memory or to LDS (Ptr: a pointer to const int in
+// either address space).
+template <int TILE, typename Ptr>
+__device__ __forceinline__ int find_seq(Ptr cu, int n, int total, int v, int lane) {
   int lo = 0, hi = n;
   while (hi - lo > 1) {
     const int step = (hi - lo + 63) / 64;

@@ -66,6 +66,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;   // query rows per work group
 constexpr int kThreads = kWaves * 64;
 constexpr int kSlots = 4;                    // LDS tile slots per kind (K, V)
+constexpr int kSeqLds = 2048;                // packed modes: sequence-table entries kept in LDS
 constexpr float kRaise = 256.0f;  // raise the stored max when a partial row sum exceeds this
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -324,6 +325,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   constexpr int kXcd = kXcds;
   __shared__ int s_unit;  // the next unit, broadcast from thread 0
   __shared__ int s_bad;   // paged: some wave met a block it cannot read
+  // Packed modes: the sequence table (cu_seqlens_q, and cu_seqlens_k or the
+  // paged lengths) is copied into LDS once per work group when it fits, so
+  // that an item finds its sequence and sizes without global loads.
+  typedef const __attribute__((address_space(3))) int lds_cint;
+  __shared__ int s_seq_a[VARLEN ? kSeqLds : 1], s_seq_b[VARLEN ? kSeqLds : 1];
+  const bool seq_in_lds = VARLEN && p.n_seqs + 1 <= kSeqLds;
+  if (seq_in_lds) {
+    for (int i = tid; i <= p.n_seqs; i += kThreads) {
+      s_seq_a[i] = p.cu_q[i];
+      s_seq_b[i] = PAGED ? (i < p.n_seqs ? p.seq_lens[i] : 0) : p.cu_k[i];
+    }
+  }
   const int G = gridDim.x;
   const int xcd = blockIdx.x % kXcd;
   int groups_before = 0;
@@ -371,14 +384,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       }
       slot = rest % p.vtiles;
       h = (rest / p.vtiles) * p.group + hg;
-      b = find_seq<kBM>(p.cu_q, p.n_seqs, p.total_q, slot, lane);
-      const int q0 = clampi(p.cu_q[b], 0, p.total_q);
-      const int q1 = clampi(p.cu_q[b + 1], q0, p.total_q);
+      // (the copy above precedes the first __syncthreads)
+      int cq0, cq1;
+      if (seq_in_lds) {
+        b = find_seq<kBM>((lds_cint*)s_seq_a, p.n_seqs, p.total_q, slot, lane);
+        cq0 = __builtin_amdgcn_readfirstlane(s_seq_a[b]);  // uniform: scalar registers
+        cq1 = __builtin_amdgcn_readfirstlane(s_seq_a[b + 1]);
+      } else {
+        b = find_seq<kBM>(p.cu_q, p.n_seqs, p.total_q, slot, lane);
+        cq0 = p.cu_q[b];
+        cq1 = p.cu_q[b + 1];
+      }
+      const int q0 = clampi(cq0, 0, p.total_q);
+      const int q1 = clampi(cq1, q0, p.total_q);
       Nq = q1 - q0;
       int k0 = 0;
       if constexpr (PAGED) {
         // the chunk's queries are the last Nq of the sequence's seq_len tokens
-        const int len = p.seq_lens[b];
+        const int len = seq_in_lds ? __builtin_amdgcn_readfirstlane(s_seq_b[b]) : p.seq_lens[b];
         bad = len < 0 || len > p.max_blocks * kBlockTokens;
         Nk = bad ? 0 : len;
         // A block id outside the pool anywhere in the sequence's table makes
@@ -394,8 +417,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
           bad = __builtin_amdgcn_ballot_w64(out) != 0;
         }
       } else {
-        k0 = clampi(p.cu_k[b], 0, p.total_k);
-        Nk = clampi(p.cu_k[b + 1], k0, p.total_k) - k0;
+        const int ck0 = seq_in_lds ? __builtin_amdgcn_readfirstlane(s_seq_b[b]) : p.cu_k[b];
+        const int ck1 = seq_in_lds ? __builtin_amdgcn_readfirstlane(s_seq_b[b + 1]) : p.cu_k[b + 1];
+        k0 = clampi(ck0, 0, p.total_k);
+        Nk = clampi(ck1, k0, p.total_k) - k0;
       }
       const int off = slot - (q0 / kBM + b);
       const int ntl = (Nq + kBM - 1) / kBM;

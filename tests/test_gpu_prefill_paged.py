@@ -101,6 +101,18 @@ def test_negative_scale_chunked_prefill():
     check(out, O, lse, L, "bf16", "chunked prefill, scale -0.09")
 
 
+def test_more_sequences_than_the_lds_table():
+    # past 2047 sequences the kernel reads cu_seqlens_q and the lengths from
+    # global memory rather than from its LDS copy
+    rng = np.random.default_rng(3095)
+    lens = [int(x) for x in rng.integers(1, 60, size=2100)]
+    chunks = [int(rng.integers(0, n + 1)) for n in lens]
+    inp = _make(lens, chunks, 2, 1, 64, 3095)
+    out, lse = _run(inp, 0.125, 0)
+    O, L = _oracle(inp, 0.125, 0)
+    check(out, O, lse, L, "bf16", "2100 sequences")
+
+
 def test_one_new_token_matches_decode():
     lens = [40, 700, 1234, 16]
     inp = _make(lens, [1] * 4, 8, 2, 128, 3100)

@@ -67,6 +67,17 @@ def test_non_positive_scale_packed(scale):
     check(out, O, lse, L, "bf16", f"packed scale {scale}")
 
 
+def test_more_sequences_than_the_lds_table():
+    # past 2047 sequences the kernel searches cu_seqlens in global memory
+    # rather than in its LDS copy
+    rng = np.random.default_rng(2060)
+    lens = [int(x) for x in rng.integers(0, 40, size=2100)]
+    q, k, v, cu_q, cu_k = workloads.make_packed(lens, lens, 2, 1, 64, 2060)
+    out, lse = _run(q, k, v, cu_q, cu_k, True, 0, 0.125)
+    O, L = oracle.attention_varlen(q, k, v, cu_q.numpy(), cu_k.numpy(), 0.125, True, 0)
+    check(out, O, lse, L, "bf16", "2100 packed sequences")
+
+
 def test_rows_outside_every_sequence_are_not_written():
     # the sequences cover rows 3 .. 3+sum-1 of a longer q; the rest keep a sentinel
     lens = [70, 300]
