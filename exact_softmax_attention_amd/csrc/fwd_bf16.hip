@@ -106,6 +106,9 @@ struct Params {
   int slot;      // this launch's slot of scheduling counters
   unsigned tag;  // and its tag (see claim_unit)
   int pairing;  // work units are pairs of query tiles (see the schedule)
+  // dense: query heads of one KV head that a work item holds (1: one head;
+  // 2, 4 or 8: kBM / gpack positions of each, one head per wave group)
+  int gpack;
   float sl2;  // scale * log2(e): scores are kept in the base-2 domain
   // packed sequences: boundaries of the query and key rows of each sequence,
   // the total rows of each tensor, and the schedule's tile slots per head
@@ -132,16 +135,17 @@ enum Mode { kDense = 0, kVarlen = 1, kPaged = 2 };
 constexpr int kBlockTokens = 16;  // tokens per cache block
 constexpr int kChunkTiles = 128;  // paged: 64-key tiles per key chunk (8192 keys)
 
-// Key tiles (64 keys) that query rows [i0, i0 + kBM) of a sequence with Nq
+// Key tiles (64 keys) that query rows [i0, i0 + rows) of a sequence with Nq
 // queries and Nk keys may see: [t_begin, t_begin + n_tiles).  i0 may be
 // negative (packed sequences' tiles end at the sequence's last row).
 struct TileRange {
   int t_begin, n_tiles;
 };
-__device__ __forceinline__ TileRange tile_range(int i0, int Nq, int Nk, int causal, int window) {
+__device__ __forceinline__ TileRange tile_range(int i0, int Nq, int Nk, int causal, int window,
+                                                int rows = kBM) {
   const int delta = Nk - Nq;
   int kv_end = Nk;
-  if (causal) kv_end = min(Nk, i0 + kBM + delta);
+  if (causal) kv_end = min(Nk, i0 + rows + delta);
   int kv_begin = 0;
   if (window > 0) kv_begin = max(0, max(i0, 0) + delta - window + 1);  // rows below 0 do not exist
   TileRange r;
@@ -344,6 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
   const int Gx = (G - xcd + kXcd - 1) / kXcd;
   const int nq = p.n_qtiles;
   const int per_head = p.pairing ? (nq + 1) / 2 : nq;
+  const int gp = (MODE == kDense && p.gpack > 1) ? p.gpack : 1;  // query heads per item
   const int units = VARLEN ? p.total : p.total / nq * per_head;
   const int first = (int)((int64_t)units * groups_before / G);
   const int last = (int)((int64_t)units * (groups_before + Gx) / G);
@@ -441,10 +446,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       k_tok0 = k0;
       lse0 = (int64_t)h * p.total_q + q0;
     } else {
+      // Grouped heads (gp > 1): the item holds positions [i0, i0 + kBM / gp)
+      // of the gp query heads that share a KV head, kWaves / gp waves per
+      // head, so its key range is that of kBM / gp positions (less of the
+      // causal diagonal and of a window's edge computed for nothing)
       qt = p.pairing ? (e == 0 ? nq - 1 - j : j) : nq - 1 - (per_head - 1 - j);
-      i0 = qt * kBM;
-      b = bh / p.Hq;
-      h = bh - b * p.Hq;
+      i0 = qt * (kBM / gp);
+      const int nhb = p.Hq / gp;  // head blocks
+      b = bh / nhb;
+      h = (bh - b * nhb) * gp + wave / (kWaves / gp);  // this wave's query head
       Nq = p.Nq;
       Nk = p.Nk;
       q_tok0 = (int64_t)b * Nq;
@@ -452,11 +462,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       lse0 = ((int64_t)b * p.Hq + h) * Nq;
     }
     const int hk = h / p.group;
-    const int qw0 = i0 + wave * kRowsPerWave;
+    const int qw0 = i0 + (wave % (kWaves / gp)) * kRowsPerWave;  // this wave's first row
     const int delta = Nk - Nq;
 
     static_assert(T::BN == 64, "tile_range counts 64-key tiles");
-    const TileRange tr_ = tile_range(i0, Nq, Nk, p.causal, p.window);
+    const TileRange tr_ = tile_range(i0, Nq, Nk, p.causal, p.window, kBM / gp);
     int t_begin = tr_.t_begin;
     int n_tiles = tr_.n_tiles;
     bool split = false;  // paged: this unit does one chunk of the item's tiles
@@ -1189,8 +1199,12 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.Nk = a.Nk;
   p.causal = a.causal;
   p.window = a.window;
-  p.n_qtiles = (a.Nq + kBM - 1) / kBM;
-  p.total = (int)fwd_bf16_grid(a.B, a.Hq, a.Nq);
+  // GQA with 2, 4 or 8 query heads per KV head: items of kBM / G positions
+  // of all G heads (never more work units than fwd_bf16_grid counts)
+  p.gpack = (p.group == 2 || p.group == 4 || p.group == 8) ? p.group : 1;
+  const int rows = kBM / p.gpack;
+  p.n_qtiles = (a.Nq + rows - 1) / rows;
+  p.total = (int)((long long)a.B * (a.Hq / p.gpack) * p.n_qtiles);
   p.sl2 = a.scale * kLog2e;
   if (p.total == 0) return hipSuccess;
   // pair query tiles when there are enough pairs to fill the CUs
