@@ -107,7 +107,8 @@ struct Params {
   unsigned tag;  // and its tag (see claim_unit)
   int pairing;  // work units are pairs of query tiles (see the schedule)
   // dense: query heads of one KV head that a work item holds (1: one head;
-  // 2, 4 or 8: kBM / gpack positions of each, one head per wave group)
+  // 2, 4 or 8, dividing the group: kBM / gpack positions of each, one head
+  // per group of kWaves / gpack waves)
   int gpack;
   float sl2;  // scale * log2(e): scores are kept in the base-2 domain
   // packed sequences: boundaries of the query and key rows of each sequence,
@@ -447,9 +448,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
       lse0 = (int64_t)h * p.total_q + q0;
     } else {
       // Grouped heads (gp > 1): the item holds positions [i0, i0 + kBM / gp)
-      // of the gp query heads that share a KV head, kWaves / gp waves per
-      // head, so its key range is that of kBM / gp positions (less of the
-      // causal diagonal and of a window's edge computed for nothing)
+      // of gp query heads that share a KV head (gp divides the group),
+      // kWaves / gp waves per head, so its key range is that of kBM / gp
+      // positions (less of the causal diagonal and of a window's edge
+      // computed for nothing)
       qt = p.pairing ? (e == 0 ? nq - 1 - j : j) : nq - 1 - (per_head - 1 - j);
       i0 = qt * (kBM / gp);
       const int nhb = p.Hq / gp;  // head blocks
@@ -1199,9 +1201,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.Nk = a.Nk;
   p.causal = a.causal;
   p.window = a.window;
-  // GQA with 2, 4 or 8 query heads per KV head: items of kBM / G positions
-  // of all G heads (never more work units than fwd_bf16_grid counts)
-  p.gpack = (p.group == 2 || p.group == 4 || p.group == 8) ? p.group : 1;
+  // grouped heads: an item holds kBM / gpack positions of gpack query heads
+  // that share a KV head, gpack the largest of 8, 4, 2 dividing the group
+  // (never more work units than fwd_bf16_grid counts)
+  p.gpack = p.group % 8 == 0 ? 8 : p.group % 4 == 0 ? 4 : p.group % 2 == 0 ? 2 : 1;
   const int rows = kBM / p.gpack;
   p.n_qtiles = (a.Nq + rows - 1) / rows;
   p.total = (int)((long long)a.B * (a.Hq / p.gpack) * p.n_qtiles);
