@@ -38,6 +38,13 @@ SMALL = [
     (1, 5, 0, 2, 1, 64, False, 0),
     (1, 333, 333, 2, 2, 128, True, 333),
     (3, 200, 200, 6, 3, 64, True, 0),
+    # groups wider than a work item's head count (8, 4 or 2 of the group's
+    # heads per item, 256 / that many positions each): MQA 32 and 16 query
+    # heads, a group of 12 and of 6, with windows, ragged lengths, Nq < Nk
+    (1, 300, 300, 32, 1, 128, True, 0),
+    (2, 257, 400, 16, 1, 64, True, 50),
+    (1, 333, 333, 12, 1, 128, True, 77),
+    (1, 100, 130, 12, 2, 128, False, 0),
 ]
 
 
