@@ -1,8 +1,9 @@
 """GPU parity where element offsets pass 2**31: the kernels' address arithmetic.
 
-A prefill and a backward pass whose Q, O, dO and dQ hold more than 2**31
-elements (rows past 524288 of 32 heads of 128 sit beyond it), and a paged
-decode whose cache blocks sit past element 2**31 of the pool, each checked
+A prefill (dense and packed) and a backward pass whose Q, O, dO and dQ hold
+more than 2**31 elements (rows past 524288 of 32 heads of 128 sit beyond it),
+and a paged decode and chunked prefill whose cache blocks sit past element
+2**31 of the pool, each checked
 against the fp64 oracle on the rows, keys and sequences that straddle the
 boundary.  A 32-bit product anywhere in the addressing would read or write the
 wrong rows (and, for the decode, NaN blocks).
@@ -19,7 +20,8 @@ import torch
 
 import oracle
 import workloads
-from exact_softmax_attention_amd import attn_bwd, attn_decode_paged, attn_fwd
+from exact_softmax_attention_amd import (attn_bwd, attn_decode_paged, attn_fwd, attn_fwd_varlen,
+                                         attn_prefill_paged)
 from tests.parity import check, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -125,3 +127,56 @@ def test_backward_past_2_31_elements():
             rv_sum = rv_sum + rv[W - 1: W - 1 + (k1 - k0)]
         _check_grad(dk_c[:, hk], rk_sum, f"large backward dk hk{hk}")
         _check_grad(dv_c[:, hk], rv_sum, f"large backward dv hk{hk}")
+
+
+def test_packed_prefill_past_2_31_elements():
+    # three packed sequences of 557056 tokens in all; the third starts at row
+    # 500000, so its rows from 24288 on lie past element 2**31
+    lens = [300000, 200000, 57056]
+    Hq, Hkv, d, W, seed = 32, 8, 128, 4096, 7304
+    print("large packed prefill: generating inputs", flush=True)
+    q, k, v, cu_q, cu_k = workloads.make_packed(lens, lens, Hq, Hkv, d, seed)
+    scale = 1.0 / np.sqrt(d)
+    out, lse = attn_fwd_varlen(q.cuda(), k.cuda(), v.cuda(), cu_q.cuda(), cu_k.cuda(), causal=True,
+                               window=W, scale=scale)
+    torch.cuda.synchronize()
+    print("large packed prefill: kernel done", flush=True)
+    first = _E31 // (Hq * d)
+    # (sequence, local rows [a, b)): each sequence's first and last rows, and
+    # the third's rows around the boundary
+    spans = [(0, 0, 40), (0, lens[0] - 40, lens[0]), (1, 0, 40), (1, lens[1] - 40, lens[1]),
+             (2, 0, 40), (2, first - 500000 - 64, first - 500000 + 64), (2, lens[2] - 40, lens[2])]
+    for s, a, b in spans:
+        t0 = int(cu_q[s])
+        c = max(0, a - W + 1)
+        for h in (0, 9, 31):
+            O, L = oracle.attention_head(q[t0 + a: t0 + b, h], k[t0 + c: t0 + b, h // 4],
+                                         v[t0 + c: t0 + b, h // 4], scale, True, W)
+            check(out[t0 + a: t0 + b, h].cpu(), O, lse[h, t0 + a: t0 + b].cpu(), L, "bf16",
+                  f"large packed prefill seq {s} rows {a}..{b} head {h}")
+
+
+def test_chunked_prefill_blocks_past_2_31_elements():
+    # the chunked prefill over a pool laid out as in the decode case
+    lens, chunks = [3001, 700, 4096, 2500], [512, 700, 1, 1000]
+    Hq, Hkv, d, seed = 32, 8, 128, 7305
+    nblk = sum((n + 15) // 16 for n in lens)
+    maxb = max((n + 15) // 16 for n in lens)
+    print("large chunked prefill: generating inputs", flush=True)
+    inp = workloads.make_prefill_paged(lens, chunks, Hq, Hkv, d, 16, nblk, maxb, seed)
+    num_blocks = 135000
+    shift = _E31 // (16 * Hkv * d) - nblk // 2
+    table = inp["block_table"].clone()
+    table[table >= 0] += shift
+    kc = torch.full((num_blocks, 16, Hkv, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    kc[shift: shift + nblk] = inp["kcache"].cuda()
+    vc[shift: shift + nblk] = inp["vcache"].cuda()
+    scale = 1.0 / np.sqrt(d)
+    out, lse = attn_prefill_paged(inp["q"].cuda(), kc, vc, table.cuda(), inp["seq_lens"].cuda(),
+                                  inp["cu_seqlens_q"].cuda(), scale=scale)
+    torch.cuda.synchronize()
+    print("large chunked prefill: kernel done", flush=True)
+    O, L = oracle.prefill_paged(inp["q"], inp["kcache"], inp["vcache"], inp["block_table"],
+                                inp["seq_lens"], inp["cu_seqlens_q"], scale)
+    check(out.cpu(), O, lse.cpu(), L, "bf16", "large chunked prefill")
