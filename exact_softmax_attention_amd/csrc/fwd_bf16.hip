@@ -1011,9 +1011,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const Params p) {
 // softmax states), taken in one pass: the running (m, sum, O) of a row is
 // rescaled whenever a chunk raises its maximum, so a row's chunks are read in
 // one round of loads.  One work group per (schedule slot, query head); a wave
-// takes 8 rows at a time, the lanes along the features, with the loads of all
-// their chunks (up to 4 at a time) in flight together; the partials are read
-// once, with non-temporal loads.  A NaN partial (a block the first pass could
+// takes 8 (D = 128) or 16 (D = 64) rows at a time, 4 features per lane, with
+// the loads of all their chunks (up to 4 at a time) in flight together; the
+// partials are read once, with non-temporal loads.  A NaN partial (a block the first pass could
 // not read) gives NaN.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(const Params p) {
@@ -1034,39 +1034,45 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const Params p) {
   const int c0 = tr.t_begin / p.chunk_tiles;
   const int c1 = (tr.t_begin + tr.n_tiles - 1) / p.chunk_tiles;
   if (c1 == c0) return;  // written directly by the first pass
-  constexpr int F = D / 64;  // features per lane
-  constexpr int R = 8;       // rows of a wave in flight together
-  constexpr int CG = 4;      // chunks whose loads are issued together
-  typedef float fF __attribute__((ext_vector_type(F)));
+  // lanes along the features, 4 per lane (16-byte loads): LPR lanes per
+  // row, RPI rows per load instruction, R rows of a wave in flight together
+  constexpr int LPR = D / 4;
+  constexpr int RPI = 64 / LPR;
+  constexpr int RI = 4;       // load instructions per chunk
+  constexpr int R = RI * RPI;
+  constexpr int CG = 4;       // chunks whose loads are issued together
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const int sub = lane % LPR, rsub = lane / LPR;
   const int64_t base = (int64_t)(h * p.vtiles + slot) * p.chunks * kBM;
   const int64_t q_row = (int64_t)p.Hq * D;
   const int nrows = min(kBM, Nq - qt * kBM);
   for (int r0 = wave * R; r0 < nrows; r0 += 4 * R) {
-    float m[R], sum[R];
-    fF o[R];
-    bool nan[R];
+    float m[RI], sum[RI];
+    f4 o[RI];
+    bool nan[RI];
   #pragma unroll
-    for (int i = 0; i < R; ++i) {
+    for (int i = 0; i < RI; ++i) {
       m[i] = kNegInf;
       sum[i] = 0.f;
-      o[i] = fF{};
+      o[i] = f4{};
       nan[i] = false;
     }
     for (int cb = c0; cb <= c1; cb += CG) {
-      float l[R][CG];
-      fF v[R][CG];
+      float l[RI][CG];
+      f4 v[RI][CG];
   #pragma unroll
-      for (int i = 0; i < R; ++i)
+      for (int i = 0; i < RI; ++i)
   #pragma unroll
         for (int j = 0; j < CG; ++j) {
-          const bool ok = cb + j <= c1 && r0 + i < nrows;
-          const int64_t pr = base + (int64_t)(cb + j) * kBM + r0 + i;
+          const int r = r0 + i * RPI + rsub;
+          const bool ok = cb + j <= c1 && r < nrows;
+          const int64_t pr = base + (int64_t)(cb + j) * kBM + r;
           l[i][j] = ok ? __builtin_nontemporal_load(p.part_lse + pr) : kNegInf;
-          v[i][j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const fF*>(p.part_o + pr * D + lane * F))
-                       : fF{};
+          v[i][j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(p.part_o + pr * D + sub * 4))
+                       : f4{};
         }
   #pragma unroll
-      for (int i = 0; i < R; ++i)
+      for (int i = 0; i < RI; ++i)
   #pragma unroll
         for (int j = 0; j < CG; ++j) {
           const float lj = l[i][j];
@@ -1080,17 +1086,16 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const Params p) {
         }
     }
   #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      if (r0 + i >= nrows) break;
+    for (int i = 0; i < RI; ++i) {
+      const int r = r0 + i * RPI + rsub;
+      if (r >= nrows) continue;
       const float inv = nan[i] ? __builtin_nanf("") : sum[i] > 0.f ? 1.f / sum[i] : 0.f;
-      const int row = qt * kBM + r0 + i;
-      uint16_t* op = p.o + ((int64_t)q0 + row) * q_row + (int64_t)h * D + lane * F;
-      if constexpr (F == 2) {
-        *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(o[i][0] * inv, o[i][1] * inv);
-      } else {
-        *op = (uint16_t)(pack_bf16x2(o[i][0] * inv, 0.f) & 0xffffu);
-      }
-      if (lane == 0 && p.lse != nullptr)
+      const int row = qt * kBM + r;
+      u32x2 w;
+      w[0] = pack_bf16x2(o[i][0] * inv, o[i][1] * inv);
+      w[1] = pack_bf16x2(o[i][2] * inv, o[i][3] * inv);
+      *reinterpret_cast<u32x2*>(p.o + ((int64_t)q0 + row) * q_row + (int64_t)h * D + sub * 4) = w;
+      if (sub == 0 && p.lse != nullptr)
         p.lse[(int64_t)h * p.total_q + q0 + row] =
             nan[i] ? __builtin_nanf("") : sum[i] > 0.f ? m[i] + fast_log2(sum[i]) * kLn2 : kNegInf;
     }
