@@ -6,7 +6,9 @@ and a paged decode and chunked prefill whose cache blocks sit past element
 2**31 of the pool, each checked
 against the fp64 oracle on the rows, keys and sequences that straddle the
 boundary.  A 32-bit product anywhere in the addressing would read or write the
-wrong rows (and, for the decode, NaN blocks).
+wrong rows (and, for the decode, NaN blocks).  The merge of two partial
+results is checked where its 16-byte piece indices pass 2**31, which its
+64-bit variant serves.
 
 The sliding window keeps the GPU work small and every result local: a query
 row sees only the W keys ending at its own position, so the oracle runs on a
@@ -21,7 +23,7 @@ import torch
 import oracle
 import workloads
 from exact_softmax_attention_amd import (attn_bwd, attn_decode_paged, attn_fwd, attn_fwd_varlen,
-                                         attn_prefill_paged)
+                                         attn_merge, attn_prefill_paged)
 from tests.parity import check, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -180,3 +182,34 @@ def test_chunked_prefill_blocks_past_2_31_elements():
     O, L = oracle.prefill_paged(inp["q"], inp["kcache"], inp["vcache"], inp["block_table"],
                                 inp["seq_lens"], inp["cu_seqlens_q"], scale)
     check(out.cpu(), O, lse.cpu(), L, "bf16", "large chunked prefill")
+
+
+def test_merge_past_2_31_pieces():
+    # 4718592 rows x 32 heads x 128: 2.42e9 16-byte pieces per tensor (38.7 GB
+    # of O each), so the pieces of rows from 4194304 on have indices past 2**31
+    B, N, H, d, seed = 1, 4718592, 32, 128, 7306
+    first = _E31 // (H * (d // 8))
+    assert B * N * H * (d // 8) > _E31 and first < N
+    print("large merge: generating inputs on the device", flush=True)
+    oa = workloads.draw_normal_device(seed, 0, (B, N, H, d))
+    ob = workloads.draw_normal_device(seed, 1, (B, N, H, d))
+    la = workloads.draw_normal_device(seed, 2, (B, H, N), torch.float32)
+    lb = workloads.draw_normal_device(seed, 3, (B, H, N), torch.float32)
+    out, lse = attn_merge(oa, la, ob, lb)
+    torch.cuda.synchronize()
+    print("large merge: kernel done", flush=True)
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, N // 2, first - 2, first - 1, first, first + 1, N - 2, N - 1}
+    rows |= set(int(x) for x in rng.integers(first - 1000, N, 24))
+    rows = torch.tensor(sorted(rows), device="cuda")
+    R = rows.numel()
+    pick = lambda o: o[0].index_select(0, rows).cpu().double().numpy()       # [R, H, d]
+    pickl = lambda l: l[0].index_select(1, rows).cpu().double().numpy()      # [H, R]
+    xa, xb, xl_a, xl_b = pick(oa), pick(ob), pickl(la), pickl(lb)
+    # the oracle's merge of (m, l, acc) states with m = LSE, l = 1, acc = O
+    M, Ls, acc = oracle.merge_states(
+        (xl_a.T.reshape(-1), np.ones(R * H), xa.reshape(-1, d)),
+        (xl_b.T.reshape(-1), np.ones(R * H), xb.reshape(-1, d)))
+    want_o = (acc / Ls[:, None]).reshape(R, H, d)
+    want_l = (M + np.log(Ls)).reshape(R, H).T
+    check(pick(out), want_o, pickl(lse), want_l, "bf16", "large merge")

@@ -208,6 +208,15 @@ def draw_normal(seed: int, tag: int, shape, sub=None) -> np.ndarray:
     return out.reshape(shape)
 
 
+def draw_normal_device(seed: int, tag: int, shape, dtype=torch.bfloat16, device="cuda"):
+    """N(0,1) of ``shape`` drawn on the device by torch's generator seeded from
+    (seed, tag): for inputs too large to draw on the host (tens of GB).  The
+    values differ from ``draw_normal``'s; only their seeding matches."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([seed, tag]).generate_state(1, np.uint64)[0] >> 1))
+    return torch.randn(tuple(int(x) for x in shape), generator=g, device=device, dtype=dtype)
+
+
 def _to(x: np.ndarray, dtype: str) -> torch.Tensor:
     t = torch.from_numpy(x)
     if dtype == "bf16":
